@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the fused clip+AdamW step on one MI355X.
+
+One step = the whole per-update hot path on one batch of synthetic gradients:
+host scalars, grad_norm_partial, grad_norm_final and the fused AdamW update,
+all through the C ABI (adamw_clip_step). Inputs are resident in HBM before the
+timed region starts: four gradient buffers are generated up front and used in
+rotation. Prints one JSON line.
+
+Byte model (algorithmic, per parameter per step): norm pass reads g (4 B);
+the update reads w, g, m, v (16 B) and writes w, m, v (12 B): 32 B in all,
+28 B of it in the update kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused clip+AdamW params/s and HBM GB/s (% of peak) at n=124.4M fp32"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+UPDATE_BYTES_PER_PARAM = 28
+STEP_BYTES_PER_PARAM = 32
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_update_vec_andrea120m_pmc.md")
+KERNEL_SRC = os.path.join(ROOT, "resumable_checkpoint_state_amd", "csrc", "rcs.hip")
+
+
+def _log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per update launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle, untuned, single-threaded on this host: full-size steps of
+    the same workload until about budget_s seconds have passed."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    n = wl.n
+    w = workloads.init_params(wl).numpy()
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = workloads.grads(wl, 1).numpy()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.adamw_clip_step(w, g, m, v, steps + 1, wl.lr, wl.wd, wl.clip)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 100:
+            break
+    return {"value": n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full {wl.name} steps (n={n:,}) on one host thread, "
+                      f"{el:.1f} s"}
+
+
+def copy_calibration(gib: float, reps: int) -> None:
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    import torch
+
+    nbytes = int(gib * (1 << 30))
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="andrea120m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-ckpt", action="store_true", help="skip the pack/unpack leg")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GiB",
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the update path is per-GPU and this build "
+              "has no multi-GPU leg (see the sharding notes in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import resumable_checkpoint_state_amd as rcs
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.calibrate_copy > 0:
+        copy_calibration(args.calibrate_copy, 10)
+        return 0
+
+    wl = workloads.WORKLOADS[args.workload]
+    n = wl.n
+    dev = torch.device("cuda:0")
+    rcs.lib()
+    _log(f"[bench] workload {wl.name} n={n:,}: generating inputs on the device")
+    w = workloads.init_params(wl, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    grads = [workloads.grads(wl, t, device=dev) for t in range(1, 5)]
+    stream = torch.cuda.current_stream()
+    rcs.init(0, stream)
+    torch.cuda.synchronize()
+
+    t = 0
+
+    def step():
+        nonlocal t
+        t += 1
+        rcs.adamw_clip_step(w, grads[(t - 1) % 4], m, v, t, wl.lr, wl.wd, wl.clip,
+                            stream=stream)
+
+    _log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events recorded by the library on
+    # the stream the kernels run on
+    rcs.profile_enable(True, max(args.steps, 1))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    norm_ms, upd_ms, rec = rcs.profile_read()
+    rcs.profile_enable(False)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    _log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step "
+         f"(wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # a second pass without per-kernel events, to show their overhead
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_noev = ev0.elapsed_time(ev1) / args.steps
+
+    upd_s = upd_ms / rec / 1e3
+    norm_s = norm_ms / rec / 1e3
+    achieved = UPDATE_BYTES_PER_PARAM * n / upd_s / 1e9
+    params_per_s = n / (ms_step / 1e3)
+    model_gbps = STEP_BYTES_PER_PARAM * n / (ms_step / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": params_per_s,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0,0.02) params, N(0,1e-4) grads in the ANDREA-120M "
+                "layout, 4 gradient buffers used in rotation, inputs resident in HBM",
+        "config": {"workload": wl.name, "n_params": n, "layout": wl.layout,
+                   "lr": wl.lr, "wd": wl.wd, "clip": wl.clip, "grad_sigma": wl.grad_sigma},
+        "model_GBps": model_gbps,
+        "model_frac_of_hbm_peak": model_gbps / HBM_PEAK_GBPS,
+        "kernels_us": {"norm_partial_plus_final": norm_s * 1e6, "adamw_update": upd_s * 1e6},
+        "ms_per_step_without_kernel_events": ms_step_noev,
+        "roofline": {"bound": "hbm", "kernel": "adamw_update_vec", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(),
+                     "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
+    }
+
+    if not args.no_ckpt:
+        nb = rcs.ckpt_bytes(n)
+        buf = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+        rcs.ckpt_pack(t, w, m, v, buf, stream=stream)  # first touch of the pinned pages
+        torch.cuda.synchronize()
+        reps = 3
+        ev0.record(stream)
+        for _ in range(reps):
+            rcs.ckpt_pack(t, w, m, v, buf, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        pack_s = ev0.elapsed_time(ev1) / reps / 1e3
+        ev0.record(stream)
+        for _ in range(reps):
+            rcs.ckpt_unpack(buf, w, m, v, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        unpack_s = ev0.elapsed_time(ev1) / reps / 1e3
+        result["ckpt"] = {"bytes": nb, "pack_GBps_host_link": nb / pack_s / 1e9,
+                          "unpack_GBps_host_link": nb / unpack_s / 1e9,
+                          "pack_ms": pack_s * 1e3, "unpack_ms": unpack_s * 1e3}
+        del buf
+
+    if not args.no_cpu_baseline:
+        _log(f"[bench] CPU baseline: the oracle for about {args.cpu_seconds:.0f} s")
+        del grads
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,156 @@
+/*
+ * rcs.h -- C ABI of the MI355X (gfx950) library for one clipped AdamW update
+ * over a flat float32 parameter vector and for the step_NNNNNN.bin state.
+ *
+ * All entry points are extern "C", take plain pointers and sizes, and only
+ * enqueue work on the given HIP stream (0 = the null stream of the current
+ * device). Every array argument is caller-owned; the library never frees or
+ * retains it. Device pointers and the stream must belong to the current
+ * device. Results are valid once the stream reaches the enqueued work; the
+ * caller must not touch the arrays or host buffers before then.
+ *
+ * The only memory the library owns is a per-(device, stream) workspace of
+ * about 32 KiB (per-block float64 partial sums and the clip scalars). It is
+ * allocated by rcs_init or on the first call that needs it, never inside a
+ * later call, and lives until the process ends.
+ *
+ * Every call validates its arguments on the host before enqueuing anything and
+ * returns one of the status codes below; a negative return means nothing was
+ * enqueued (except RCS_EHIP, which reports a failed launch or copy).
+ */
+#ifndef RCS_H
+#define RCS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum rcs_status {
+    RCS_OK = 0,
+    RCS_EINVAL = -1,  /* null pointer, bad size, bad scalar, not device memory */
+    RCS_ESIZE = -2,   /* buffer length differs from 8 + 12 n, or an array is too short */
+    RCS_EHEADER = -3, /* step file header inconsistent (n <= 0, step < 0, n mismatch) */
+    RCS_EHIP = -4,    /* a HIP launch, copy or allocation failed */
+    RCS_ENOMEM = -5   /* workspace allocation failed */
+};
+
+/* Largest n the step file's int32 header can describe. */
+#define RCS_MAX_N 2147483647LL
+
+/* Human-readable text for a status code (static storage). */
+const char *rcs_strerror(int status);
+
+/* Allocates the workspace of (device, stream) ahead of time so that no later
+ * call allocates. Optional. */
+int rcs_init(int device, hipStream_t stream);
+
+/*
+ * One training update: global L2 gradient-norm clip, then decoupled-weight-
+ * decay AdamW with bias correction, in place on w, m, v.
+ *
+ * Follows "Training as a Recoverable State Transition", section "The Exact
+ * Targets of Clipping and AdamW": g is one vector; if ||g||_2 > clip it is
+ * scaled by clip/||g||, otherwise left alone; beta1 = 0.9, beta2 = 0.999,
+ * eps = 1e-8, m_hat = m/(1-beta1^t), v_hat = v/(1-beta2^t); parameters are
+ * first multiplied by (1 - lr*wd), then lr*m_hat/(sqrt(v_hat)+eps) is
+ * subtracted; decay applies to every element. The three-kernel clip split
+ * (per-block partial sums, one final reduction, one scale) is the one the
+ * backprop lesson of grow_a_language_model names in its pairing-rule table;
+ * here the scale is applied in registers inside the update and g is not
+ * written.
+ *
+ *   w, m, v  device float32[n], read and written.
+ *   g        device float32[n], read only. Must not overlap w, m or v.
+ *   n        1 .. RCS_MAX_N.
+ *   t        1-based index of this update (a fresh run starts at 1; after
+ *            ckpt_unpack returned step k, continue with t = k + 1).
+ *   lr, wd   finite; clip > 0 (+inf means never clip).
+ *
+ * Arithmetic (float32, each op rounded to nearest-even, no contraction,
+ * subnormals kept): norm = sqrt(sum of float64 squares) in float64;
+ * s = (float)(clip/norm) if norm > clip else 1; per element gp = g*s,
+ * m = 0.9f*m + 0.1f*gp, v = 0.999f*v + 0.001f*(gp*gp), mh = m/bc1,
+ * vh = v/bc2, w = w*decay - (lr*mh)/(sqrtf(vh) + 1e-8f), where
+ * bc1 = (float)(1-0.9^t), bc2 = (float)(1-0.999^t) and
+ * decay = (float)(1 - (double)lr*(double)wd) are computed on the host.
+ * If the norm is not finite the update is skipped on the device (w, m, v are
+ * left untouched); read the norm with last_grad_norm.
+ * The reduction order depends only on n, so results are deterministic.
+ * 16-byte aligned arrays take the vector path; others a scalar path with the
+ * same arithmetic.
+ */
+int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
+                    float lr, float wd, float clip, hipStream_t stream);
+
+/*
+ * The pre-clip global norm alone: sqrt(sum_i (double)g[i]^2), same kernels and
+ * order as adamw_clip_step. norm_out is device memory or pinned host memory
+ * and receives one float64 once the stream reaches this call.
+ */
+int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream);
+
+/*
+ * Copies the pre-clip norm computed by the most recent adamw_clip_step or
+ * grad_global_norm on this stream into norm_out (device or pinned host
+ * float64), in stream order. The resume lesson records this norm before the
+ * clip to detect numerical faults. RCS_EINVAL if nothing ran on the stream.
+ */
+int last_grad_norm(hipStream_t stream, double *norm_out);
+
+/*
+ * Size of a step file for n parameters: 8 + 12 n, or -1 if n <= 0 or
+ * n > RCS_MAX_N. Layout from grow_a_language_model_checkpoints, sections
+ * "Format" and "Total size": [int32 step][int32 n][n f32 w][n f32 m][n f32 v].
+ */
+int64_t ckpt_bytes(int64_t n);
+
+/*
+ * Packs the state into host_buf (buf_bytes must equal ckpt_bytes(n)):
+ * little-endian int32 step and n at offsets 0 and 4 (written by the host
+ * before returning), then w, m, v copied device-to-host at offsets 8, 8+4n,
+ * 8+8n in stream order. step is the number of completed updates (>= 0); the
+ * resume lesson saves after a complete optimizer step. host_buf should be
+ * pinned (hipHostMalloc) for the copies to be asynchronous.
+ */
+int ckpt_pack(int32_t step, int64_t n, const float *w, const float *m, const float *v,
+              void *host_buf, int64_t buf_bytes, hipStream_t stream);
+
+/*
+ * Validates a packed state and copies it host-to-device. The header is read
+ * on the host before returning, so host_buf must already hold the bytes.
+ * Rejected (nothing copied, outputs untouched): buf_bytes < 8 (RCS_ESIZE),
+ * header n <= 0 or step < 0 or n != n_expected (RCS_EHEADER), buf_bytes !=
+ * 8 + 12 n (RCS_ESIZE). On success *step_out = step and w, m, v (device
+ * float32[n_expected]) receive the arrays in stream order; continue training
+ * with t = step + 1. The checks follow the sharded-resume lesson's rule that
+ * a bad checkpoint must fail loudly rather than load silently.
+ */
+int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int32_t *step_out,
+                float *w, float *m, float *v, hipStream_t stream);
+
+/*
+ * Instrumentation: while enabled, adamw_clip_step records HIP events on its
+ * stream around the norm kernels and around the update kernel (up to
+ * max_records steps; later steps are not recorded). rcs_profile_read
+ * synchronizes those events and returns the summed milliseconds and the
+ * number of recorded steps. Enabling resets the counters.
+ */
+int rcs_profile_enable(int on, int max_records);
+int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *steps);
+
+/*
+ * Self-test of the device arithmetic the update relies on: q[i] = a[i]/b[i]
+ * and r[i] = sqrtf(a[i]) in float32 on the device, for comparison with the
+ * host's IEEE results. Device float32 arrays of n elements.
+ */
+int rcs_fp32_div_sqrt_probe(const float *a, const float *b, float *q, float *r, int64_t n,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RCS_H */

@@ -1,0 +1,200 @@
+"""Thin Python binding of librcs.so (the gfx950 clip+AdamW / step-file library).
+
+Argument marshalling only: every step of the update runs in the HIP kernels of
+csrc/rcs.hip behind the C ABI declared in include/rcs.h. PyTorch supplies the
+device memory (CUDA tensors on ROCm) and the stream
+(``torch.cuda.current_stream().cuda_stream`` is the HIP stream handle).
+
+There is no fallback: if librcs.so is missing or cannot be loaded, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._build import LIB as LIB_PATH
+from ._build import build
+
+__all__ = [
+    "RcsError", "adamw_clip_step", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
+    "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read", "fp32_div_sqrt_probe",
+    "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
+]
+
+OK, EINVAL, ESIZE, EHEADER, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
+MAX_N = 2_147_483_647
+
+
+class RcsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads librcs.so (built in-tree by build()); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python -m resumable_checkpoint_state_amd._build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, f32p = ctypes.c_void_p, ctypes.c_void_p
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.rcs_strerror.argtypes = [ctypes.c_int]
+    L.rcs_strerror.restype = ctypes.c_char_p
+    L.rcs_init.argtypes = [ctypes.c_int, vp]
+    L.rcs_init.restype = ctypes.c_int
+    L.adamw_clip_step.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, vp]
+    L.adamw_clip_step.restype = ctypes.c_int
+    L.grad_global_norm.argtypes = [f32p, i64, vp, vp]
+    L.grad_global_norm.restype = ctypes.c_int
+    L.last_grad_norm.argtypes = [vp, vp]
+    L.last_grad_norm.restype = ctypes.c_int
+    L.ckpt_bytes.argtypes = [i64]
+    L.ckpt_bytes.restype = i64
+    L.ckpt_pack.argtypes = [i32, i64, f32p, f32p, f32p, vp, i64, vp]
+    L.ckpt_pack.restype = ctypes.c_int
+    L.ckpt_unpack.argtypes = [vp, i64, i64, ctypes.POINTER(i32), f32p, f32p, f32p, vp]
+    L.ckpt_unpack.restype = ctypes.c_int
+    L.rcs_profile_enable.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.rcs_profile_enable.restype = ctypes.c_int
+    L.rcs_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.rcs_profile_read.restype = ctypes.c_int
+    L.rcs_fp32_div_sqrt_probe.argtypes = [f32p, f32p, f32p, f32p, i64, vp]
+    L.rcs_fp32_div_sqrt_probe.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().rcs_strerror(status).decode()
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise RcsError(rc, where)
+    return rc
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev_f32(t: torch.Tensor, name: str, n: int | None = None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    return t.data_ptr()
+
+
+def init(device: int | None = None, stream=None) -> None:
+    """Allocates the (device, stream) workspace ahead of the first step."""
+    dev = torch.cuda.current_device() if device is None else device
+    _check(lib().rcs_init(dev, _stream(stream)), "rcs_init")
+
+
+def adamw_clip_step(w, g, m, v, t: int, lr: float, wd: float, clip: float, stream=None) -> None:
+    """One clipped AdamW update of w, m, v in place (asynchronous on stream)."""
+    n = w.numel()
+    args = (_dev_f32(w, "w"), _dev_f32(g, "g", n), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    _check(lib().adamw_clip_step(*args, n, int(t), float(lr), float(wd), float(clip),
+                                 _stream(stream)), "adamw_clip_step")
+
+
+def _norm_out(out):
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device="cuda")
+    if out.dtype != torch.float64 or out.numel() < 1 or not out.is_contiguous():
+        raise TypeError("norm output must be a contiguous float64 tensor")
+    if not out.is_cuda and not out.is_pinned():
+        raise TypeError("norm output must be device or pinned host memory")
+    return out
+
+
+def grad_global_norm(g, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Pre-clip global L2 norm of g into a 1-element float64 tensor."""
+    gp = _dev_f32(g, "g")
+    out = _norm_out(out)
+    _check(lib().grad_global_norm(gp, g.numel(), out.data_ptr(), _stream(stream)),
+           "grad_global_norm")
+    return out
+
+
+def last_grad_norm(out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The pre-clip norm of the last update enqueued on the stream."""
+    out = _norm_out(out)
+    _check(lib().last_grad_norm(_stream(stream), out.data_ptr()), "last_grad_norm")
+    return out
+
+
+def ckpt_bytes(n: int) -> int:
+    return lib().ckpt_bytes(n)
+
+
+def step_file_name(step: int) -> str:
+    """step_NNNNNN.bin, six digits, widening past 999,999."""
+    return "step_%06d.bin" % step
+
+
+def _host_u8(buf: torch.Tensor, name: str) -> int:
+    if not isinstance(buf, torch.Tensor) or buf.is_cuda or buf.dtype != torch.uint8 \
+            or not buf.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous uint8 host tensor (pinned for async copies)")
+    return buf.data_ptr()
+
+
+def ckpt_pack(step: int, w, m, v, buf: torch.Tensor, stream=None) -> torch.Tensor:
+    """Packs [int32 step][int32 n][w][m][v] into the host tensor buf."""
+    n = w.numel()
+    ptrs = (_dev_f32(w, "w"), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    _check(lib().ckpt_pack(int(step), n, *ptrs, _host_u8(buf, "buf"), buf.numel(),
+                           _stream(stream)), "ckpt_pack")
+    return buf
+
+
+def ckpt_unpack(buf: torch.Tensor, w, m, v, stream=None) -> int:
+    """Validates buf and copies its arrays into w, m, v; returns the header step."""
+    n = w.numel()
+    ptrs = (_dev_f32(w, "w"), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    step = ctypes.c_int32(-1)
+    _check(lib().ckpt_unpack(_host_u8(buf, "buf"), buf.numel(), n, ctypes.byref(step), *ptrs,
+                             _stream(stream)), "ckpt_unpack")
+    return step.value
+
+
+def profile_enable(on: bool, max_records: int = 4096) -> None:
+    _check(lib().rcs_profile_enable(1 if on else 0, max_records), "rcs_profile_enable")
+
+
+def profile_read():
+    """(norm ms total, update ms total, recorded steps); synchronizes events."""
+    a, b, k = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(lib().rcs_profile_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(k)),
+           "rcs_profile_read")
+    return a.value, b.value, k.value
+
+
+def fp32_div_sqrt_probe(a, b, stream=None):
+    n = a.numel()
+    q = torch.empty_like(a)
+    r = torch.empty_like(a)
+    _check(lib().rcs_fp32_div_sqrt_probe(_dev_f32(a, "a"), _dev_f32(b, "b", n), q.data_ptr(),
+                                         r.data_ptr(), n, _stream(stream)),
+           "rcs_fp32_div_sqrt_probe")
+    return q, r

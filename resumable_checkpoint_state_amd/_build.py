@@ -1,0 +1,40 @@
+"""Builds librcs.so in-tree from csrc/rcs.hip with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "rcs.hip")
+LIB = os.path.join(PKG, "librcs.so")
+INCLUDE = os.path.join(ROOT, "include")
+
+# -ffp-contract=off: every float op rounds on its own (no FMA contraction).
+# Packed float32 instructions are disabled for all device code.
+# HIP's defaults are kept for correctly rounded float32 divide/sqrt and for
+# float32 subnormals (no -ffast-math, no denormal flushing).
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    p = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    return p if os.path.exists(p) else "hipcc"
+
+
+def build(extra_flags: list[str] | None = None, out: str | None = None) -> str:
+    out = out or LIB
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

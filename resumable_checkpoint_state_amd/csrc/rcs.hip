@@ -1,0 +1,623 @@
+// rcs.hip -- gfx950 kernels and the C ABI for one clipped AdamW update over a
+// flat float32 parameter vector, plus the step_NNNNNN.bin pack/unpack.
+//
+// Method sources (pages named by title, then section):
+//   * "Training as a Recoverable State Transition", section "The Exact Targets
+//     of Clipping and AdamW": global L2 clip to threshold c; AdamW with
+//     beta1 = 0.9, beta2 = 0.999, eps = 1e-8, bias correction by
+//     1 - beta^t, decay (1 - lr*wd) applied to every parameter first.
+//   * grow_a_language_model_backprop, section on the pairing rule: the clip
+//     is split into a per-block partial-sum kernel, a final-reduction kernel
+//     and a scale kernel. Here the scale is folded into the update so g is
+//     read once more and never written.
+//   * grow_a_language_model_checkpoints, sections "Format", "Region by
+//     region" and "Total size": [int32 step][int32 n][w][m][v], 8 + 12 n bytes.
+//
+// Hardware mapping (MI355X, CDNA4, 64-wide waves, 256 CUs):
+//   * grad_norm_partial: a grid fixed by n alone streams g with 16-byte loads,
+//     squares in float64 (exact for float32 inputs) into four independent
+//     accumulators per lane, reduces each wave with DPP row permutes plus two
+//     cross-row swizzles, and combines the block's waves through LDS in wave
+//     order. One float64 partial per block; no floating-point atomics, so the
+//     result depends only on n and the data.
+//   * grad_norm_final: one block sums the partials in a fixed order, takes the
+//     float64 square root and writes {norm, clip factor, apply flag}.
+//   * adamw_update: pure HBM stream (16 B read + 12 B written per element)
+//     with 16-byte loads/stores of w, g, m, v; the clip factor is read from
+//     device memory, so the host never waits between kernels.
+// No MFMA: nothing here is a contraction.
+//
+// Floating-point contract: built with -ffp-contract=off (and the pragma
+// below), correctly rounded float32 divide and square root (HIP's default),
+// and without denormal flushing, so every float32 op is one IEEE
+// round-to-nearest-even operation, matching the sequence documented in rcs.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "rcs.h"
+
+#pragma clang fp contract(off)
+
+#ifndef RCS_UPD_UNROLL
+#define RCS_UPD_UNROLL 2
+#endif
+#ifndef RCS_UPD_NT
+#define RCS_UPD_NT 1
+#endif
+#ifndef RCS_UPD_MAX_BLOCKS
+#define RCS_UPD_MAX_BLOCKS 0  // 0: one pass, one vector group per thread
+#endif
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kNormThreads = 256;
+constexpr int kNormUnroll = 4;  // float4 loads in flight per lane per iteration
+constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormUnroll;  // float4 per block-iteration
+constexpr int kNormMaxBlocks = 2048;
+constexpr int kFinalThreads = 256;
+constexpr int kUpdThreads = 256;
+constexpr int kUpdUnroll = RCS_UPD_UNROLL;
+constexpr int64_t kUpdChunk = (int64_t)kUpdThreads * kUpdUnroll;
+
+// Native 16-byte vector (the nontemporal builtins need a clang vector type).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct ClipScalars {
+    double norm;    // pre-clip global L2 norm
+    float scale;    // clip factor s
+    int32_t apply;  // 1 when the norm is finite, else the update is skipped
+};
+
+struct StepScalars {
+    float lr, bc1, bc2, decay;
+};
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ double as_double(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+    return as_double((uint32_t)lo, (uint32_t)hi);
+}
+
+// Sum over the 64 lanes; every lane ends with the same value (each step adds
+// a value to its mirror partner, and a + b == b + a exactly).
+__device__ __forceinline__ double wave_sum(double x) {
+    x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]: pairs
+    x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]: quads
+    x += dpp_f64<0x141>(x);  // row_half_mirror: 8 lanes
+    x += dpp_f64<0x140>(x);  // row_mirror: 16-lane row
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
+// Block sum in wave order; the result is valid in thread 0 only.
+template <int THREADS>
+__device__ __forceinline__ double block_sum(double x, double *lds) {
+    x = wave_sum(x);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    if (lane == 0) lds[wid] = x;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        r = lds[0];
+#pragma unroll
+        for (int i = 1; i < THREADS / kWave; ++i) r += lds[i];
+    }
+    return r;
+}
+
+__device__ __forceinline__ double sq(float x) {
+    const double d = (double)x;
+    return d * d;
+}
+
+// a1: per-block float64 partial sums of squares.
+__global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *__restrict__ g,
+                                                                  int64_t n, int vec_ok,
+                                                                  double *__restrict__ partials) {
+    __shared__ double lds[kNormThreads / kWave];
+    double acc[kNormUnroll];
+#pragma unroll
+    for (int j = 0; j < kNormUnroll; ++j) acc[j] = 0.0;
+    const int64_t nblk = gridDim.x;
+    if (vec_ok) {
+        const f32x4 *__restrict__ g4 = reinterpret_cast<const f32x4 *>(g);
+        const int64_t n4 = n >> 2;
+        for (int64_t base = (int64_t)blockIdx.x * kNormChunk; base < n4; base += nblk * kNormChunk) {
+            f32x4 x[kNormUnroll];
+#pragma unroll
+            for (int j = 0; j < kNormUnroll; ++j) {
+                const int64_t i = base + (int64_t)j * kNormThreads + threadIdx.x;
+                x[j] = (i < n4) ? __builtin_nontemporal_load(g4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < kNormUnroll; ++j) {
+                acc[j] += sq(x[j].x);
+                acc[j] += sq(x[j].y);
+                acc[j] += sq(x[j].z);
+                acc[j] += sq(x[j].w);
+            }
+        }
+        const int rem = (int)(n & 3);
+        if (blockIdx.x == 0 && (int)threadIdx.x < rem) acc[0] += sq(g[(n4 << 2) + threadIdx.x]);
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * kNormThreads + threadIdx.x; i < n;
+             i += nblk * kNormThreads)
+            acc[0] += sq(g[i]);
+    }
+    const double t = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const double b = block_sum<kNormThreads>(t, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = b;
+}
+
+// a2: one block reduces the partials, then norm, clip factor and apply flag.
+__global__ __launch_bounds__(kFinalThreads) void grad_norm_final(const double *__restrict__ partials,
+                                                                 int nparts, float clip,
+                                                                 ClipScalars *__restrict__ out) {
+    __shared__ double lds[kFinalThreads / kWave];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += kFinalThreads) acc += partials[i];
+    const double S = block_sum<kFinalThreads>(acc, lds);
+    if (threadIdx.x == 0) {
+        const double norm = sqrt(S);
+        ClipScalars r;
+        r.norm = norm;
+        r.apply = isfinite(norm) ? 1 : 0;
+        r.scale = (norm > (double)clip) ? (float)((double)clip / norm) : 1.0f;
+        *out = r;
+    }
+}
+
+// ---------------------------------------------------------------- update
+
+// The float32 op sequence of one element; every line is one rounding.
+__device__ __forceinline__ void adamw_elem(float &w, float g, float &m, float &v, float s,
+                                           const StepScalars &h) {
+    const float gp = g * s;
+    const float mi = 0.9f * m + 0.1f * gp;
+    const float vi = 0.999f * v + 0.001f * (gp * gp);
+    const float mh = mi / h.bc1;
+    const float vh = vi / h.bc2;
+    const float den = __builtin_sqrtf(vh) + 1e-8f;
+    w = w * h.decay - (h.lr * mh) / den;
+    m = mi;
+    v = vi;
+}
+
+__device__ __forceinline__ void adamw_vec4(f32x4 &w, f32x4 g, f32x4 &m, f32x4 &v, float s,
+                                           const StepScalars &h) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float ww = w[k], mm = m[k], vv = v[k];
+        adamw_elem(ww, g[k], mm, vv, s, h);
+        w[k] = ww;
+        m[k] = mm;
+        v[k] = vv;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p) {
+#if RCS_UPD_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T *p, T x) {
+#if RCS_UPD_NT
+    __builtin_nontemporal_store(x, p);
+#else
+    *p = x;
+#endif
+}
+
+// a3: fused clip-scale + AdamW, 16-byte vectors of w, g, m, v.
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
+    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ v, int64_t n, const ClipScalars *__restrict__ sc, StepScalars h) {
+    if (!sc->apply) return;
+    const float s = sc->scale;
+    const int64_t n4 = n >> 2;
+    const int64_t nblk = gridDim.x;
+    for (int64_t base = (int64_t)blockIdx.x * kUpdChunk; base < n4; base += nblk * kUpdChunk) {
+        f32x4 wr[kUpdUnroll], gr[kUpdUnroll], mr[kUpdUnroll], vr[kUpdUnroll];
+#pragma unroll
+        for (int j = 0; j < kUpdUnroll; ++j) {
+            const int64_t i = base + (int64_t)j * kUpdThreads + threadIdx.x;
+            if (i < n4) {
+                gr[j] = ld_stream(g + i);
+                wr[j] = ld_stream(w + i);
+                mr[j] = ld_stream(m + i);
+                vr[j] = ld_stream(v + i);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kUpdUnroll; ++j) {
+            const int64_t i = base + (int64_t)j * kUpdThreads + threadIdx.x;
+            if (i < n4) {
+                adamw_vec4(wr[j], gr[j], mr[j], vr[j], s, h);
+                st_stream(w + i, wr[j]);
+                st_stream(m + i, mr[j]);
+                st_stream(v + i, vr[j]);
+            }
+        }
+    }
+    // the n % 4 trailing elements
+    const int rem = (int)(n & 3);
+    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
+        const int64_t i = (n4 << 2) + threadIdx.x;
+        float *wf = reinterpret_cast<float *>(w);
+        float *mf = reinterpret_cast<float *>(m);
+        float *vf = reinterpret_cast<float *>(v);
+        const float *gf = reinterpret_cast<const float *>(g);
+        float ww = wf[i], mm = mf[i], vv = vf[i];
+        adamw_elem(ww, gf[i], mm, vv, s, h);
+        wf[i] = ww;
+        mf[i] = mm;
+        vf[i] = vv;
+    }
+}
+
+// a3 for arrays that are not all 16-byte aligned: same arithmetic per element.
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_scalar(
+    float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, const ClipScalars *__restrict__ sc, StepScalars h) {
+    if (!sc->apply) return;
+    const float s = sc->scale;
+    const int64_t stride = (int64_t)gridDim.x * kUpdThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kUpdThreads + threadIdx.x; i < n; i += stride) {
+        float ww = w[i], mm = m[i], vv = v[i];
+        adamw_elem(ww, g[i], mm, vv, s, h);
+        w[i] = ww;
+        m[i] = mm;
+        v[i] = vv;
+    }
+}
+
+__global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restrict__ a,
+                                                           const float *__restrict__ b,
+                                                           float *__restrict__ q,
+                                                           float *__restrict__ r, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+        q[i] = a[i] / b[i];
+        r[i] = __builtin_sqrtf(a[i]);
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+struct Workspace {
+    double *partials = nullptr;      // kNormMaxBlocks float64
+    ClipScalars *scalars = nullptr;  // one record
+    bool has_norm = false;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+struct Profile {
+    bool on = false;
+    int max_records = 0;
+    int next = 0;
+    std::vector<hipEvent_t> ev;  // 3 per recorded step
+} g_prof;
+
+int get_workspace(hipStream_t stream, Workspace **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto key = std::make_pair(dev, stream);
+    auto it = g_ws.find(key);
+    if (it == g_ws.end()) {
+        void *p = nullptr;
+        const size_t bytes = (size_t)kNormMaxBlocks * sizeof(double) + 256;
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return RCS_ENOMEM;
+        }
+        Workspace ws;
+        ws.partials = static_cast<double *>(p);
+        ws.scalars = reinterpret_cast<ClipScalars *>(static_cast<char *>(p) +
+                                                     (size_t)kNormMaxBlocks * sizeof(double));
+        it = g_ws.emplace(key, ws).first;
+    }
+    *out = &it->second;
+    return RCS_OK;
+}
+
+// The range [p, p + bytes) must lie inside one device allocation.
+int check_device_range(const void *p, int64_t bytes) {
+    if (p == nullptr) return RCS_EINVAL;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) == hipSuccess && base) {
+        const char *lo = static_cast<const char *>(base);
+        const char *q = static_cast<const char *>(p);
+        if (q < lo || q + bytes > lo + size) return RCS_ESIZE;
+        return RCS_OK;
+    }
+    (void)hipGetLastError();
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return RCS_EINVAL;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return RCS_EINVAL;
+    return RCS_OK;
+}
+
+bool overlaps(const void *a, const void *b, int64_t bytes) {
+    const char *x = static_cast<const char *>(a);
+    const char *y = static_cast<const char *>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int norm_blocks(int64_t n) {
+    const int64_t per_block = kNormChunk * 4;  // floats per block-iteration
+    int64_t b = (n + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > kNormMaxBlocks) b = kNormMaxBlocks;
+    return (int)b;
+}
+
+int launch_norm(const float *g, int64_t n, float clip, Workspace *ws, hipStream_t stream) {
+    const int nb = norm_blocks(n);
+    hipLaunchKernelGGL(grad_norm_partial, dim3(nb), dim3(kNormThreads), 0, stream, g, n,
+                       aligned16(g) ? 1 : 0, ws->partials);
+    hipLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream,
+                       (const double *)ws->partials, nb, clip, ws->scalars);
+    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
+}
+
+int launch_update(float *w, const float *g, float *m, float *v, int64_t n, const ClipScalars *sc,
+                  const StepScalars &h, hipStream_t stream) {
+    if (aligned16(w) && aligned16(g) && aligned16(m) && aligned16(v)) {
+        const int64_t n4 = n >> 2;
+        int64_t blocks = (n4 + kUpdChunk - 1) / kUpdChunk;
+        if (blocks < 1) blocks = 1;
+        if (RCS_UPD_MAX_BLOCKS > 0 && blocks > RCS_UPD_MAX_BLOCKS) blocks = RCS_UPD_MAX_BLOCKS;
+        hipLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream,
+                           reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
+                           reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n, sc, h);
+    } else {
+        int64_t blocks = (n + kUpdThreads - 1) / kUpdThreads;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(adamw_update_scalar, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
+                           stream, w, g, m, v, n, sc, h);
+    }
+    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
+}
+
+void put_le32(unsigned char *p, int32_t x) {
+    const uint32_t u = (uint32_t)x;
+    for (int k = 0; k < 4; ++k) p[k] = (unsigned char)((u >> (8 * k)) & 0xffu);
+}
+
+int32_t get_le32(const unsigned char *p) {
+    uint32_t u = 0;
+    for (int k = 0; k < 4; ++k) u |= (uint32_t)p[k] << (8 * k);
+    return (int32_t)u;
+}
+
+bool valid_n(int64_t n) { return n >= 1 && n <= RCS_MAX_N; }
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+const char *rcs_strerror(int status) {
+    switch (status) {
+        case RCS_OK: return "ok";
+        case RCS_EINVAL: return "invalid argument (null pointer, bad size or scalar, or not device memory)";
+        case RCS_ESIZE: return "size mismatch (buffer is not 8 + 12 n bytes, or an array is shorter than n)";
+        case RCS_EHEADER: return "step file header rejected (n <= 0, step < 0 or n differs from the expected n)";
+        case RCS_EHIP: return "HIP launch, copy or allocation failed";
+        case RCS_ENOMEM: return "workspace allocation failed";
+        default: return "unknown status";
+    }
+}
+
+int rcs_init(int device, hipStream_t stream) {
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return RCS_EHIP;
+    if (hipSetDevice(device) != hipSuccess) {
+        (void)hipGetLastError();
+        return RCS_EINVAL;
+    }
+    Workspace *ws = nullptr;
+    const int rc = get_workspace(stream, &ws);
+    (void)hipSetDevice(prev);
+    return rc;
+}
+
+int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t, float lr,
+                    float wd, float clip, hipStream_t stream) {
+    if (!valid_n(n) || t < 1) return RCS_EINVAL;
+    if (!std::isfinite(lr) || !std::isfinite(wd) || std::isnan(clip) || !(clip > 0.0f))
+        return RCS_EINVAL;
+    const int64_t bytes = 4 * n;
+    int rc;
+    if ((rc = check_device_range(w, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(g, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
+    if (overlaps(w, g, bytes) || overlaps(w, m, bytes) || overlaps(w, v, bytes) ||
+        overlaps(g, m, bytes) || overlaps(g, v, bytes) || overlaps(m, v, bytes))
+        return RCS_EINVAL;
+    Workspace *ws = nullptr;
+    if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
+
+    // a0: host scalars, float64 then one rounding each.
+    StepScalars h;
+    h.lr = lr;
+    h.bc1 = (float)(1.0 - std::pow(0.9, (double)t));
+    h.bc2 = (float)(1.0 - std::pow(0.999, (double)t));
+    h.decay = (float)(1.0 - (double)lr * (double)wd);
+
+    hipEvent_t *ev = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (g_prof.on && g_prof.next < g_prof.max_records) ev = &g_prof.ev[3 * g_prof.next++];
+    }
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    if ((rc = launch_norm(g, n, clip, ws, stream)) != RCS_OK) return rc;
+    if (ev) (void)hipEventRecord(ev[1], stream);
+    rc = launch_update(w, g, m, v, n, ws->scalars, h, stream);
+    if (ev) (void)hipEventRecord(ev[2], stream);
+    ws->has_norm = true;
+    return rc;
+}
+
+int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream) {
+    if (!valid_n(n) || norm_out == nullptr) return RCS_EINVAL;
+    int rc;
+    if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
+    Workspace *ws = nullptr;
+    if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
+    if ((rc = launch_norm(g, n, INFINITY, ws, stream)) != RCS_OK) return rc;
+    ws->has_norm = true;
+    if (hipMemcpyAsync(norm_out, &ws->scalars->norm, sizeof(double), hipMemcpyDefault, stream) !=
+        hipSuccess)
+        return RCS_EHIP;
+    return RCS_OK;
+}
+
+int last_grad_norm(hipStream_t stream, double *norm_out) {
+    if (norm_out == nullptr) return RCS_EINVAL;
+    Workspace *ws = nullptr;
+    int rc;
+    if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
+    if (!ws->has_norm) return RCS_EINVAL;
+    if (hipMemcpyAsync(norm_out, &ws->scalars->norm, sizeof(double), hipMemcpyDefault, stream) !=
+        hipSuccess)
+        return RCS_EHIP;
+    return RCS_OK;
+}
+
+int64_t ckpt_bytes(int64_t n) { return valid_n(n) ? 8 + 12 * n : -1; }
+
+int ckpt_pack(int32_t step, int64_t n, const float *w, const float *m, const float *v,
+              void *host_buf, int64_t buf_bytes, hipStream_t stream) {
+    if (!valid_n(n) || step < 0 || host_buf == nullptr) return RCS_EINVAL;
+    if (buf_bytes != ckpt_bytes(n)) return RCS_ESIZE;
+    const int64_t bytes = 4 * n;
+    int rc;
+    if ((rc = check_device_range(w, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
+    unsigned char *b = static_cast<unsigned char *>(host_buf);
+    put_le32(b, step);
+    put_le32(b + 4, (int32_t)n);
+    if (hipMemcpyAsync(b + 8, w, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(b + 8 + bytes, m, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(b + 8 + 2 * bytes, v, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return RCS_EHIP;
+    return RCS_OK;
+}
+
+int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int32_t *step_out,
+                float *w, float *m, float *v, hipStream_t stream) {
+    if (host_buf == nullptr || step_out == nullptr || !valid_n(n_expected)) return RCS_EINVAL;
+    if (buf_bytes < 8) return RCS_ESIZE;
+    const unsigned char *b = static_cast<const unsigned char *>(host_buf);
+    const int32_t step = get_le32(b);
+    const int32_t n = get_le32(b + 4);
+    if (n <= 0 || step < 0) return RCS_EHEADER;
+    if ((int64_t)n != n_expected) return RCS_EHEADER;
+    if (buf_bytes != 8 + 12 * (int64_t)n) return RCS_ESIZE;
+    const int64_t bytes = 4 * (int64_t)n;
+    int rc;
+    if ((rc = check_device_range(w, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
+    if (hipMemcpyAsync(w, b + 8, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(m, b + 8 + bytes, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(v, b + 8 + 2 * bytes, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return RCS_EHIP;
+    *step_out = step;
+    return RCS_OK;
+}
+
+int rcs_profile_enable(int on, int max_records) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.on = false;
+    g_prof.next = 0;
+    g_prof.max_records = 0;
+    if (!on) return RCS_OK;
+    if (max_records < 1 || max_records > (1 << 20)) return RCS_EINVAL;
+    g_prof.ev.resize((size_t)3 * max_records);
+    for (auto &e : g_prof.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            (void)hipGetLastError();
+            return RCS_EHIP;
+        }
+    }
+    g_prof.max_records = max_records;
+    g_prof.on = true;
+    return RCS_OK;
+}
+
+int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *steps) {
+    if (!norm_ms_total || !update_ms_total || !steps) return RCS_EINVAL;
+    std::lock_guard<std::mutex> lk(g_mu);
+    double a = 0.0, b = 0.0;
+    for (int i = 0; i < g_prof.next; ++i) {
+        hipEvent_t *e = &g_prof.ev[3 * i];
+        if (hipEventSynchronize(e[2]) != hipSuccess) return RCS_EHIP;
+        float x = 0.f, y = 0.f;
+        if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess ||
+            hipEventElapsedTime(&y, e[1], e[2]) != hipSuccess)
+            return RCS_EHIP;
+        a += x;
+        b += y;
+    }
+    *norm_ms_total = a;
+    *update_ms_total = b;
+    *steps = g_prof.next;
+    return RCS_OK;
+}
+
+int rcs_fp32_div_sqrt_probe(const float *a, const float *b, float *q, float *r, int64_t n,
+                            hipStream_t stream) {
+    if (n < 1 || n > RCS_MAX_N) return RCS_EINVAL;
+    const int64_t bytes = 4 * n;
+    int rc;
+    if ((rc = check_device_range(a, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(b, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(q, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(r, bytes)) != RCS_OK) return rc;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fp32_div_sqrt_probe, dim3((unsigned)blocks), dim3(256), 0, stream, a, b, q,
+                       r, n);
+    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+"""The C-ABI library: it loads, exports every entry point its header declares,
+and rejects bad arguments on the host before touching the device. None of these
+calls launch GPU work, so they run without a GPU."""
+import ctypes
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import resumable_checkpoint_state_amd as rcs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rcs.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rcs.LIB_PATH):
+        rcs.build()
+    return rcs.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ["adamw_clip_step", "grad_global_norm", "ckpt_pack", "ckpt_unpack",
+                     "ckpt_bytes", "last_grad_norm", "rcs_strerror"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_library_is_built_for_gfx950():
+    data = open(rcs.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_ckpt_bytes_closed_form(L):
+    for n in [1, 3, 262_144, 12_800_000, 124_356_864, 2_000_000_000, 2**31 - 1]:
+        assert rcs.ckpt_bytes(n) == 8 + 12 * n
+    for n in [0, -5, 2**31]:
+        assert rcs.ckpt_bytes(n) == -1
+
+
+def test_strerror_covers_codes(L):
+    for code in [rcs.OK, rcs.EINVAL, rcs.ESIZE, rcs.EHEADER, rcs.EHIP, rcs.ENOMEM]:
+        assert rcs.strerror(code) and rcs.strerror(code) != "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: rejected before any device check
+
+
+@pytest.mark.parametrize("n,t,lr,wd,clip", [
+    (0, 1, 1e-3, 0.0, 1.0), (-1, 1, 1e-3, 0.0, 1.0), (2**31, 1, 1e-3, 0.0, 1.0),
+    (16, 0, 1e-3, 0.0, 1.0), (16, -3, 1e-3, 0.0, 1.0), (16, 1, float("nan"), 0.0, 1.0),
+    (16, 1, float("inf"), 0.0, 1.0), (16, 1, 1e-3, float("nan"), 1.0),
+    (16, 1, 1e-3, 0.0, 0.0), (16, 1, 1e-3, 0.0, -1.0), (16, 1, 1e-3, 0.0, float("nan")),
+])
+def test_adamw_clip_step_rejects_bad_scalars(L, n, t, lr, wd, clip):
+    rc = L.adamw_clip_step(FAKE, FAKE, FAKE, FAKE, n, t, lr, wd, clip, None)
+    assert rc == rcs.EINVAL
+
+
+def test_null_pointers_rejected(L):
+    assert L.adamw_clip_step(None, None, None, None, 16, 1, 1e-3, 0.0, 1.0, None) == rcs.EINVAL
+    assert L.grad_global_norm(None, 16, None, None) == rcs.EINVAL
+    assert L.last_grad_norm(None, None) == rcs.EINVAL
+    buf = (ctypes.c_uint8 * 20)()
+    assert L.ckpt_pack(1, 1, FAKE, FAKE, FAKE, None, 20, None) == rcs.EINVAL
+    assert L.ckpt_pack(-1, 1, FAKE, FAKE, FAKE, buf, 20, None) == rcs.EINVAL
+    assert L.ckpt_pack(1, 1, FAKE, FAKE, FAKE, buf, 19, None) == rcs.ESIZE
+    step = ctypes.c_int32(-7)
+    assert L.ckpt_unpack(None, 20, 1, ctypes.byref(step), FAKE, FAKE, FAKE, None) == rcs.EINVAL
+    assert L.ckpt_unpack(buf, 20, 1, None, FAKE, FAKE, FAKE, None) == rcs.EINVAL
+    assert L.ckpt_unpack(buf, 20, 0, ctypes.byref(step), FAKE, FAKE, FAKE, None) == rcs.EINVAL
+
+
+def _packed(step, n):
+    return bytearray(struct.pack("<ii", step, n) + bytes(12 * n))
+
+
+@pytest.mark.parametrize("case,want", [
+    ("short_header", rcs.ESIZE), ("truncated", rcs.ESIZE), ("extended", rcs.ESIZE),
+    ("n_zero", rcs.EHEADER), ("n_negative", rcs.EHEADER), ("n_mismatch", rcs.EHEADER),
+    ("step_negative", rcs.EHEADER),
+])
+def test_unpack_header_faults_rejected_before_any_copy(L, case, want):
+    """Fault injection on the host: every malformed buffer is rejected by the
+    header checks, which run before any device pointer is looked at, and the
+    step output is left untouched."""
+    n = 16
+    b = _packed(5, n)
+    if case == "short_header":
+        b = b[:7]
+    elif case == "truncated":
+        b = b[:-1]
+    elif case == "extended":
+        b = b + b"\0"
+    elif case == "n_zero":
+        b[4:8] = struct.pack("<i", 0)
+    elif case == "n_negative":
+        b[4:8] = struct.pack("<i", -n)
+    elif case == "n_mismatch":
+        b[4:8] = struct.pack("<i", n + 1)
+    elif case == "step_negative":
+        b[0:4] = struct.pack("<i", -1)
+    arr = (ctypes.c_uint8 * len(b)).from_buffer(b)
+    step = ctypes.c_int32(-7)
+    rc = L.ckpt_unpack(arr, len(b), n, ctypes.byref(step), FAKE, FAKE, FAKE, None)
+    assert rc == want
+    assert step.value == -7
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    a = torch.zeros(8)
+    with pytest.raises(TypeError):
+        rcs.adamw_clip_step(a, a, a, a, 1, 1e-3, 0.0, 1.0)
+    with pytest.raises(TypeError):
+        rcs.grad_global_norm(a)
+
+
+def test_step_file_name():
+    assert rcs.step_file_name(80) == "step_000080.bin"
+    assert rcs.step_file_name(112700) == "step_112700.bin"
+    assert rcs.step_file_name(1234567) == "step_1234567.bin"

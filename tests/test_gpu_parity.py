@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar (from the method's precision): the float64 pre-clip norm within 1e-12
+relative; w, m, v within 2 float32 ulp per element after every step (the
+float32 op sequence is the same on both sides, so they are expected to be
+bit-identical unless the two float64 norms round the clip factor apart);
+headers, layout and packed bytes bit-exact; a packed-and-resumed run
+bit-identical to the straight run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import resumable_checkpoint_state_amd as rcs
+import workloads
+from util import bits, max_ulp
+
+pytestmark = pytest.mark.gpu
+
+NORM_RTOL = 1e-12
+ULP_TOL = 2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rcs.lib()
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+def _gpu_norm():
+    return float(rcs.last_grad_norm().cpu())
+
+
+def _check_state(w, m, v, ow, om, ov, ctx):
+    for name, a, b in (("w", w, ow), ("m", m, om), ("v", v, ov)):
+        d = max_ulp(_host(a), b)
+        assert d <= ULP_TOL, f"{ctx}: {name} max ulp distance {d}"
+
+
+# ---------------------------------------------------------------- device arithmetic
+
+def test_fp32_divide_and_sqrt_are_correctly_rounded(dev):
+    rng = np.random.default_rng(0)
+    n = 1 << 20
+    a = rng.standard_normal(n).astype(np.float32) * np.float32(1e3)
+    b = rng.standard_normal(n).astype(np.float32)
+    e = rng.integers(-149, 127, n)
+    a[: n // 4] = np.ldexp(rng.random(n // 4) + 0.5, e[: n // 4]).astype(np.float32)
+    b[n // 4: n // 2] = np.ldexp(rng.random(n // 4) + 0.5, e[n // 4: n // 2]).astype(np.float32)
+    a[:64] = np.float32(1.4e-45) * np.arange(1, 65, dtype=np.float32)  # subnormal numerators
+    b[b == 0] = 1.0
+    q, r = rcs.fp32_div_sqrt_probe(torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev))
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        q_ref = a / b
+        r_ref = np.sqrt(np.abs(a))
+    assert (bits(_host(q)) == bits(q_ref)).all()
+    pos = a >= 0
+    assert (bits(_host(r))[pos] == bits(r_ref)[pos]).all()
+
+
+# ---------------------------------------------------------------- norm
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 63, 64, 65, 1023, 4096, 4097, 16387, 262_147,
+                               1_000_003, 40_000_003])
+def test_norm_parity_sizes(dev, n):
+    g = workloads.custom(100, n, 0.01, device=dev)
+    out = rcs.grad_global_norm(g)
+    torch.cuda.synchronize()
+    ref = oracle.grad_norm(_host(g))
+    got = float(out.cpu())
+    assert abs(got - ref) <= NORM_RTOL * ref, (n, got, ref)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_norm_parity_unaligned(dev, offset):
+    n = 100_003
+    base = workloads.custom(101, n + offset, 1.0, device=dev)
+    g = base[offset:]
+    out = rcs.grad_global_norm(g)
+    torch.cuda.synchronize()
+    ref = oracle.grad_norm(_host(g).copy())
+    assert abs(float(out.cpu()) - ref) <= NORM_RTOL * ref
+
+
+def test_norm_exact_power_of_two_cases(dev):
+    n = 1 << 18
+    g = torch.full((n,), 2.0 ** -6, device=dev)
+    assert float(rcs.grad_global_norm(g).cpu()) == 8.0
+    g.fill_(2.0 ** -10)
+    assert float(rcs.grad_global_norm(g).cpu()) == 0.5
+    g.zero_()
+    g[12345] = -3.25
+    assert float(rcs.grad_global_norm(g).cpu()) == 3.25
+    g.zero_()
+    assert float(rcs.grad_global_norm(g).cpu()) == 0.0
+
+
+def test_norm_into_pinned_host(dev):
+    g = workloads.custom(102, 70_001, 1.0, device=dev)
+    out = torch.zeros(1, dtype=torch.float64, pin_memory=True)
+    rcs.grad_global_norm(g, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.grad_norm(_host(g))
+    assert abs(float(out[0]) - ref) <= NORM_RTOL * ref
+
+
+def test_clip_exact_power_of_two_update(dev):
+    """n = 2^18, g = 2^-6: norm 8, s = 0.125 exactly on both sides, so the
+    whole update must be bit-identical."""
+    n = 1 << 18
+    w = workloads.custom(103, n, 0.02, device=dev)
+    g = torch.full((n,), 2.0 ** -6, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rcs.adamw_clip_step(w, g, m, v, 1, 3e-3, 0.01, 1.0)
+    oracle.adamw_clip_step(ow, _host(g), om, ov, 1, 3e-3, 0.01, 1.0)
+    torch.cuda.synchronize()
+    assert _gpu_norm() == 8.0
+    for a, b in ((w, ow), (m, om), (v, ov)):
+        assert (bits(_host(a)) == bits(b)).all()
+
+
+# ---------------------------------------------------------------- update
+
+def _run_parity(dev, wl, steps, n=None, scale=1.0):
+    n = wl.n if n is None else n
+    w = workloads.init_params(wl, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = torch.empty(n, device=dev)
+    diffs = 0
+    for t in range(1, steps + 1):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        if scale != 1.0:
+            g.mul_(scale)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        gn = _gpu_norm()
+        rc, on = oracle.adamw_clip_step(ow, _host(g), om, ov, t, wl.lr, wl.wd, wl.clip)
+        assert rc == oracle.OK
+        assert abs(gn - on) <= NORM_RTOL * on, (t, gn, on)
+        _check_state(w, m, v, ow, om, ov, f"{wl.name} n={n} t={t}")
+        diffs += int((bits(_host(w)) != bits(ow)).sum())
+    return w, m, v, diffs
+
+
+def test_update_parity_flat262k_all_80_steps(dev):
+    wl = workloads.WORKLOADS["flat262k"]
+    _, _, _, diffs = _run_parity(dev, wl, wl.steps)
+    print(f"flat262k: {diffs} w elements off by 1-2 ulp over {wl.steps} steps")
+
+
+@pytest.mark.parametrize("n", [1, 3, 5, 511, 513, 4099, 65_537])
+def test_update_parity_ragged_sizes(dev, n):
+    wl = workloads.WORKLOADS["flat262k"]
+    _run_parity(dev, wl, 3, n=n, scale=50.0)
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_update_parity_unaligned_scalar_path(dev, offset):
+    wl = workloads.WORKLOADS["flat262k"]
+    n = 50_001
+    mk = lambda: torch.zeros(n + offset, device=dev)  # noqa: E731
+    W, G, M, V = mk(), mk(), mk(), mk()
+    w, g, m, v = W[offset:], G[offset:], M[offset:], V[offset:]
+    w.copy_(workloads.init_params(wl, device=dev, n=n))
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in (1, 2, 3):
+        g.copy_(workloads.grads(wl, t, device=dev, n=n)).mul_(10.0)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        oracle.adamw_clip_step(ow, _host(g).copy(), om, ov, t, wl.lr, wl.wd, wl.clip)
+        torch.cuda.synchronize()
+        _check_state(w, m, v, ow, om, ov, f"unaligned offset={offset} t={t}")
+
+
+def test_update_parity_andrea12m(dev):
+    _run_parity(dev, workloads.WORKLOADS["andrea12m"], 3)
+
+
+def test_update_parity_andrea12m_both_clip_branches(dev):
+    """Steps 1, 2 stay under the threshold (s = 1, g used as is); step 3 has
+    the outliers and clips."""
+    wl = workloads.WORKLOADS["andrea12m_b"]
+    n = wl.n
+    w = workloads.init_params(wl, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    norms = []
+    for t in (1, 2, 3):
+        g = workloads.grads(wl, t, device=dev)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        _, on = oracle.adamw_clip_step(ow, _host(g), om, ov, t, wl.lr, wl.wd, wl.clip)
+        norms.append(on)
+        assert abs(_gpu_norm() - on) <= NORM_RTOL * on
+        _check_state(w, m, v, ow, om, ov, f"andrea12m_b t={t}")
+    assert norms[0] < wl.clip and norms[1] < wl.clip and norms[2] > wl.clip
+
+
+def test_update_parity_andrea120m_full_size(dev):
+    _run_parity(dev, workloads.WORKLOADS["andrea120m"], 2)
+
+
+def test_update_parity_stress_subnormals_full_size(dev):
+    wl = workloads.WORKLOADS["andrea120m_stress"]
+    w, m, v, _ = _run_parity(dev, wl, 2)
+    mh = _host(m)
+    sub = (mh != 0) & (np.abs(mh) < np.float32(1.1754944e-38))
+    assert sub.sum() > 0, "stress grads should leave subnormal first moments"
+
+
+def test_nonfinite_norm_skips_update(dev):
+    n = 10_000
+    w = workloads.custom(104, n, 0.02, device=dev)
+    m = workloads.custom(105, n, 0.01, device=dev)
+    v = workloads.custom(106, n, 0.01, device=dev).abs_()
+    before = [_host(x).copy() for x in (w, m, v)]
+    for bad in (float("inf"), float("nan")):
+        g = workloads.custom(107, n, 1.0, device=dev)
+        g[777] = bad
+        rcs.adamw_clip_step(w, g, m, v, 4, 3e-3, 0.01, 1.0)
+        norm = _gpu_norm()
+        assert not np.isfinite(norm)
+        for x, b in zip((w, m, v), before):
+            assert (bits(_host(x)) == bits(b)).all()
+
+
+# ---------------------------------------------------------------- pack / resume
+
+def _pinned(nbytes):
+    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+
+def test_pack_bytes_match_oracle_layout(dev):
+    n = 262_147
+    w = workloads.custom(108, n, 1.0, device=dev)
+    m = workloads.custom(109, n, 1.0, device=dev)
+    v = workloads.custom(110, n, 1.0, device=dev)
+    buf = _pinned(rcs.ckpt_bytes(n))
+    rcs.ckpt_pack(80, w, m, v, buf)
+    torch.cuda.synchronize()
+    _, ob = oracle.ckpt_pack(80, _host(w), _host(m), _host(v))
+    assert buf.numpy().tobytes() == ob.tobytes()
+
+
+def test_unpack_rejects_and_leaves_device_untouched(dev):
+    n = 1000
+    w = workloads.custom(111, n, 1.0, device=dev)
+    keep = _host(w).copy()
+    buf = _pinned(rcs.ckpt_bytes(n))
+    rcs.ckpt_pack(3, w, w.clone(), w.clone(), buf)
+    torch.cuda.synchronize()
+    bad = torch.cat([buf, torch.zeros(1, dtype=torch.uint8)])
+    m2, v2 = torch.zeros_like(w), torch.zeros_like(w)
+    with pytest.raises(rcs.RcsError):
+        rcs.ckpt_unpack(bad, w, m2, v2)
+    with pytest.raises(rcs.RcsError):
+        rcs.ckpt_unpack(buf[:-1].clone(), w, m2, v2)
+    with pytest.raises(rcs.RcsError):
+        rcs.ckpt_unpack(buf, w[:-1], m2[:-1], v2[:-1])
+    torch.cuda.synchronize()
+    assert (bits(_host(w)) == bits(keep)).all() and not m2.any() and not v2.any()
+
+
+def _straight_vs_resumed(dev, wl, steps, pack_at, n=None):
+    n = wl.n if n is None else n
+    w0 = workloads.init_params(wl, device=dev, n=n)
+    g = torch.empty(n, device=dev)
+    # straight
+    w, (m, v) = w0.clone(), workloads.zeros_like_state(n, device=dev)
+    for t in range(1, steps + 1):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+    # run to pack_at, pack, drop the state, unpack into fresh buffers, resume
+    w2, (m2, v2) = w0.clone(), workloads.zeros_like_state(n, device=dev)
+    for t in range(1, pack_at + 1):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w2, g, m2, v2, t, wl.lr, wl.wd, wl.clip)
+    buf = _pinned(rcs.ckpt_bytes(n))
+    rcs.ckpt_pack(pack_at, w2, m2, v2, buf)
+    torch.cuda.synchronize()
+    del w2, m2, v2
+    w3, m3, v3 = (torch.full((n,), float("nan"), device=dev) for _ in range(3))
+    step = rcs.ckpt_unpack(buf, w3, m3, v3)
+    assert step == pack_at
+    for t in range(step + 1, steps + 1):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w3, g, m3, v3, t, wl.lr, wl.wd, wl.clip)
+    out_a, out_b = _pinned(rcs.ckpt_bytes(n)), _pinned(rcs.ckpt_bytes(n))
+    rcs.ckpt_pack(steps, w, m, v, out_a)
+    rcs.ckpt_pack(steps, w3, m3, v3, out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b), f"{wl.name}: resumed state differs from straight run"
+    return w, m, v, out_a
+
+
+def test_resume_bit_identical_flat262k(dev):
+    wl = workloads.WORKLOADS["flat262k"]
+    w, m, v, packed = _straight_vs_resumed(dev, wl, wl.steps, 40)
+    # the packed step_000080.bin: header and size fixed by the layout
+    assert packed.numel() == 3_145_736
+    rc, step, n = oracle.ckpt_header(packed.numpy())
+    assert (rc, step, n) == (oracle.OK, 80, wl.n)
+    # and the GPU trajectory stays within the bar of the oracle's
+    ow = _host(workloads.init_params(wl, device=dev)).copy()
+    om, ov = np.zeros(wl.n, np.float32), np.zeros(wl.n, np.float32)
+    for t in range(1, wl.steps + 1):
+        oracle.adamw_clip_step(ow, _host(workloads.grads(wl, t, device=dev)), om, ov, t,
+                               wl.lr, wl.wd, wl.clip)
+    _check_state(w, m, v, ow, om, ov, "flat262k after 80 steps")
+
+
+def test_resume_bit_identical_andrea12m(dev):
+    wl = workloads.WORKLOADS["andrea12m"]
+    _straight_vs_resumed(dev, wl, 20, 10)
+
+
+def test_resume_bit_identical_stress_full_size(dev):
+    wl = workloads.WORKLOADS["andrea120m_stress"]
+    _, _, _, packed = _straight_vs_resumed(dev, wl, wl.steps, 100)
+    assert packed.numel() == 1_492_282_376
