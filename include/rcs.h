@@ -133,12 +133,14 @@ int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int
 
 /*
  * Instrumentation: while enabled, adamw_clip_step records HIP events on its
- * stream around the norm kernels and around the update kernel (up to
- * max_records steps; later steps are not recorded). rcs_profile_read
- * synchronizes those events and returns the summed milliseconds and the
- * number of recorded steps. Enabling resets the counters.
+ * stream around the norm kernels and around the update kernel, on one call in
+ * `every` (the first call after enabling is recorded), up to max_records
+ * recorded calls. rcs_profile_read synchronizes those events and returns the
+ * summed milliseconds and the number of recorded calls. Enabling (or
+ * disabling) discards earlier records. Events are created here, not in the
+ * recorded calls.
  */
-int rcs_profile_enable(int on, int max_records);
+int rcs_profile_enable(int on, int max_records, int every);
 int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *steps);
 
 /*

@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
     L.ckpt_pack.restype = ctypes.c_int
     L.ckpt_unpack.argtypes = [vp, i64, i64, ctypes.POINTER(i32), f32p, f32p, f32p, vp]
     L.ckpt_unpack.restype = ctypes.c_int
-    L.rcs_profile_enable.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.rcs_profile_enable.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.rcs_profile_enable.restype = ctypes.c_int
     L.rcs_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -178,8 +178,9 @@ def ckpt_unpack(buf: torch.Tensor, w, m, v, stream=None) -> int:
     return step.value
 
 
-def profile_enable(on: bool, max_records: int = 4096) -> None:
-    _check(lib().rcs_profile_enable(1 if on else 0, max_records), "rcs_profile_enable")
+def profile_enable(on: bool, max_records: int = 4096, every: int = 1) -> None:
+    """Per-kernel HIP events inside adamw_clip_step on one call in `every`."""
+    _check(lib().rcs_profile_enable(1 if on else 0, max_records, every), "rcs_profile_enable")
 
 
 def profile_read():

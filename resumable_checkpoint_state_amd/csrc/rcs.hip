@@ -14,17 +14,23 @@
 //     region" and "Total size": [int32 step][int32 n][w][m][v], 8 + 12 n bytes.
 //
 // Hardware mapping (MI355X, CDNA4, 64-wide waves, 256 CUs):
-//   * grad_norm_partial: a grid fixed by n alone streams g with 16-byte loads,
-//     squares in float64 (exact for float32 inputs) into four independent
-//     accumulators per lane, reduces each wave with DPP row permutes plus two
-//     cross-row swizzles, and combines the block's waves through LDS in wave
-//     order. One float64 partial per block; no floating-point atomics, so the
-//     result depends only on n and the data.
-//   * grad_norm_final: one block sums the partials in a fixed order, takes the
-//     float64 square root and writes {norm, clip factor, apply flag}.
-//   * adamw_update: pure HBM stream (16 B read + 12 B written per element)
-//     with 16-byte loads/stores of w, g, m, v; the clip factor is read from
-//     device memory, so the host never waits between kernels.
+//   * grad_norm_partial: a grid fixed by n alone streams g with 16-byte
+//     loads, squares in float64 (exact for float32 inputs) into four
+//     independent accumulators per lane, reduces each wave with DPP row
+//     permutes plus two cross-row swizzles, and combines the block's waves
+//     through LDS in wave order: one float64 partial per block. The last
+//     320 MB of g are read with cache-allocating loads so that the part of g
+//     still in the 256 MB last-level cache serves the update's second read;
+//     the rest streams.
+//   * grad_norm_final: one 1024-lane block sums the partials in a fixed tree,
+//     takes the float64 square root and writes {norm, clip factor, apply
+//     flag}. No floating-point atomics anywhere, so the result depends only
+//     on n and the data. (A single kernel whose last block does this step
+//     needs a device-scope release per block, which on this chip costs an L2
+//     write-back per block and measured slower than the extra launch.)
+//   * adamw_update_vec: pure HBM stream (16 B read + 12 B written per element)
+//     with 16-byte streaming loads/stores of w, g, m, v; the clip factor is
+//     read from device memory, so the host never waits between kernels.
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -46,25 +52,33 @@
 
 #pragma clang fp contract(off)
 
+// Launch-shape knobs (overridable at build time for sweeps).
+#ifndef RCS_UPD_THREADS
+#define RCS_UPD_THREADS 256
+#endif
 #ifndef RCS_UPD_UNROLL
-#define RCS_UPD_UNROLL 2
+#define RCS_UPD_UNROLL 1
 #endif
 #ifndef RCS_UPD_NT
 #define RCS_UPD_NT 1
 #endif
-#ifndef RCS_UPD_MAX_BLOCKS
-#define RCS_UPD_MAX_BLOCKS 0  // 0: one pass, one vector group per thread
+// Bytes at the end of g that the norm pass reads with ordinary (cache-
+// allocating) loads so that the update, which reads g again right after,
+// finds them in the last-level cache; the rest is read with streaming loads.
+// A negative value reads all of g with ordinary loads.
+#ifndef RCS_NORM_CACHED_TAIL_BYTES
+#define RCS_NORM_CACHED_TAIL_BYTES (320LL << 20)
 #endif
 
 namespace {
 
 constexpr int kWave = 64;
 constexpr int kNormThreads = 256;
-constexpr int kNormUnroll = 4;  // float4 loads in flight per lane per iteration
-constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormUnroll;  // float4 per block-iteration
+constexpr int kNormUnroll = 4;  // 16-byte loads in flight per lane per iteration
+constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormUnroll;  // vectors per block-iteration
 constexpr int kNormMaxBlocks = 2048;
-constexpr int kFinalThreads = 256;
-constexpr int kUpdThreads = 256;
+constexpr int kFinalThreads = 1024;
+constexpr int kUpdThreads = RCS_UPD_THREADS;
 constexpr int kUpdUnroll = RCS_UPD_UNROLL;
 constexpr int64_t kUpdChunk = (int64_t)kUpdThreads * kUpdUnroll;
 
@@ -129,9 +143,11 @@ __device__ __forceinline__ double sq(float x) {
     return d * d;
 }
 
-// a1: per-block float64 partial sums of squares.
+// a1: per-block float64 partial sums of squares. The first nt_limit4 vectors
+// are read with streaming loads, the rest with cache-allocating loads.
 __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *__restrict__ g,
                                                                   int64_t n, int vec_ok,
+                                                                  int64_t nt_limit4,
                                                                   double *__restrict__ partials) {
     __shared__ double lds[kNormThreads / kWave];
     double acc[kNormUnroll];
@@ -143,10 +159,18 @@ __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *_
         const int64_t n4 = n >> 2;
         for (int64_t base = (int64_t)blockIdx.x * kNormChunk; base < n4; base += nblk * kNormChunk) {
             f32x4 x[kNormUnroll];
+            if (base < nt_limit4) {
 #pragma unroll
-            for (int j = 0; j < kNormUnroll; ++j) {
-                const int64_t i = base + (int64_t)j * kNormThreads + threadIdx.x;
-                x[j] = (i < n4) ? __builtin_nontemporal_load(g4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < kNormUnroll; ++j) {
+                    const int64_t i = base + (int64_t)j * kNormThreads + threadIdx.x;
+                    x[j] = (i < n4) ? __builtin_nontemporal_load(g4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kNormUnroll; ++j) {
+                    const int64_t i = base + (int64_t)j * kNormThreads + threadIdx.x;
+                    x[j] = (i < n4) ? g4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
 #pragma unroll
             for (int j = 0; j < kNormUnroll; ++j) {
@@ -168,14 +192,18 @@ __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *_
     if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
-// a2: one block reduces the partials, then norm, clip factor and apply flag.
+// a2: one block sums the partials (lane i takes partials i and i + 1024, then
+// the fixed wave/LDS tree), takes the float64 square root and writes
+// {norm, clip factor, apply flag}.
+static_assert(kNormMaxBlocks <= 2 * kFinalThreads, "final kernel reads two partials per lane");
 __global__ __launch_bounds__(kFinalThreads) void grad_norm_final(const double *__restrict__ partials,
                                                                  int nparts, float clip,
                                                                  ClipScalars *__restrict__ out) {
     __shared__ double lds[kFinalThreads / kWave];
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < nparts; i += kFinalThreads) acc += partials[i];
-    const double S = block_sum<kFinalThreads>(acc, lds);
+    const int i0 = threadIdx.x, i1 = threadIdx.x + kFinalThreads;
+    const double x0 = (i0 < nparts) ? partials[i0] : 0.0;
+    const double x1 = (i1 < nparts) ? partials[i1] : 0.0;
+    const double S = block_sum<kFinalThreads>(x0 + x1, lds);
     if (threadIdx.x == 0) {
         const double norm = sqrt(S);
         ClipScalars r;
@@ -320,6 +348,8 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 struct Profile {
     bool on = false;
     int max_records = 0;
+    int every = 1;       // record one step in `every`
+    int64_t calls = 0;   // adamw_clip_step calls since enabling
     int next = 0;
     std::vector<hipEvent_t> ev;  // 3 per recorded step
 } g_prof;
@@ -337,10 +367,10 @@ int get_workspace(hipStream_t stream, Workspace **out) {
             (void)hipGetLastError();
             return RCS_ENOMEM;
         }
+        char *base = static_cast<char *>(p);
         Workspace ws;
-        ws.partials = static_cast<double *>(p);
-        ws.scalars = reinterpret_cast<ClipScalars *>(static_cast<char *>(p) +
-                                                     (size_t)kNormMaxBlocks * sizeof(double));
+        ws.partials = reinterpret_cast<double *>(base);
+        ws.scalars = reinterpret_cast<ClipScalars *>(base + (size_t)kNormMaxBlocks * sizeof(double));
         it = g_ws.emplace(key, ws).first;
     }
     *out = &it->second;
@@ -384,10 +414,18 @@ int norm_blocks(int64_t n) {
     return (int)b;
 }
 
+// First vector index the norm pass reads with cache-allocating loads.
+int64_t norm_nt_limit4(int64_t n) {
+    const int64_t n4 = n >> 2;
+    if (RCS_NORM_CACHED_TAIL_BYTES < 0) return 0;
+    const int64_t tail4 = (int64_t)RCS_NORM_CACHED_TAIL_BYTES / 16;
+    return n4 > tail4 ? n4 - tail4 : 0;
+}
+
 int launch_norm(const float *g, int64_t n, float clip, Workspace *ws, hipStream_t stream) {
     const int nb = norm_blocks(n);
     hipLaunchKernelGGL(grad_norm_partial, dim3(nb), dim3(kNormThreads), 0, stream, g, n,
-                       aligned16(g) ? 1 : 0, ws->partials);
+                       aligned16(g) ? 1 : 0, norm_nt_limit4(n), ws->partials);
     hipLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream,
                        (const double *)ws->partials, nb, clip, ws->scalars);
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
@@ -399,7 +437,6 @@ int launch_update(float *w, const float *g, float *m, float *v, int64_t n, const
         const int64_t n4 = n >> 2;
         int64_t blocks = (n4 + kUpdChunk - 1) / kUpdChunk;
         if (blocks < 1) blocks = 1;
-        if (RCS_UPD_MAX_BLOCKS > 0 && blocks > RCS_UPD_MAX_BLOCKS) blocks = RCS_UPD_MAX_BLOCKS;
         hipLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream,
                            reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
                            reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n, sc, h);
@@ -483,7 +520,8 @@ int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int
     hipEvent_t *ev = nullptr;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        if (g_prof.on && g_prof.next < g_prof.max_records) ev = &g_prof.ev[3 * g_prof.next++];
+        if (g_prof.on && (g_prof.calls++ % g_prof.every) == 0 && g_prof.next < g_prof.max_records)
+            ev = &g_prof.ev[3 * g_prof.next++];
     }
     if (ev) (void)hipEventRecord(ev[0], stream);
     if ((rc = launch_norm(g, n, clip, ws, stream)) != RCS_OK) return rc;
@@ -564,15 +602,17 @@ int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int
     return RCS_OK;
 }
 
-int rcs_profile_enable(int on, int max_records) {
+int rcs_profile_enable(int on, int max_records, int every) {
     std::lock_guard<std::mutex> lk(g_mu);
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
     g_prof.ev.clear();
     g_prof.on = false;
     g_prof.next = 0;
+    g_prof.calls = 0;
     g_prof.max_records = 0;
     if (!on) return RCS_OK;
-    if (max_records < 1 || max_records > (1 << 20)) return RCS_EINVAL;
+    if (max_records < 1 || max_records > (1 << 20) || every < 1) return RCS_EINVAL;
+    g_prof.every = every;
     g_prof.ev.resize((size_t)3 * max_records);
     for (auto &e : g_prof.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
