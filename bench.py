@@ -79,6 +79,52 @@ def cpu_baseline(wl, budget_s: float):
                       f"{el:.1f} s"}
 
 
+def async_pack_overlap(rcs, step, stream, w, m, v, buf, n, k=60):
+    """K update steps alone, then the same K steps with an asynchronous pack
+    (device snapshot + copy-stream drain) issued before them; the pack's
+    host-link time should hide behind the steps."""
+    import torch
+
+    snap = torch.empty(rcs.ckpt_snapshot_bytes(n) // 4, device=w.device)
+    copy_stream = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rcs.ckpt_pack_async(0, w, m, v, snap, buf, compute_stream=stream, copy_stream=copy_stream)
+    rcs.ckpt_pack_wait(snap)  # first touch
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(k):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    alone = e0.elapsed_time(e1)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    rcs.ckpt_pack_async(0, w, m, v, snap, buf, compute_stream=stream, copy_stream=copy_stream)
+    for _ in range(k):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    both_wall = (time.perf_counter() - t0) * 1e3
+    with_pack = e0.elapsed_time(e1)
+    return {"async_pack_steps": k, "steps_ms_alone": alone,
+            "steps_ms_with_async_pack": with_pack, "wall_ms_steps_and_pack": both_wall}
+
+
+def file_write_rate(rcs, buf):
+    """Atomic write of one packed step file (tmp + fsync + rename) to TMPDIR."""
+    import shutil
+    import tempfile
+
+    d = tempfile.mkdtemp(prefix="rcs_bench_", dir=os.environ.get("TMPDIR", "/tmp"))
+    try:
+        t0 = time.perf_counter()
+        rcs.ckpt_file_write(d, buf)
+        dt = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    return {"file_write_GBps_with_fsync": buf.numel() / dt / 1e9, "file_write_ms": dt * 1e3}
+
+
 def copy_calibration(gib: float, reps: int) -> None:
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -232,6 +278,8 @@ def main() -> int:
         result["ckpt"] = {"bytes": nb, "pack_GBps_host_link": nb / pack_s / 1e9,
                           "unpack_GBps_host_link": nb / unpack_s / 1e9,
                           "pack_ms": pack_s * 1e3, "unpack_ms": unpack_s * 1e3}
+        result["ckpt"].update(async_pack_overlap(rcs, step, stream, w, m, v, buf, n))
+        result["ckpt"].update(file_write_rate(rcs, buf))
         del buf
 
     if not args.no_cpu_baseline:

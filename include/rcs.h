@@ -34,7 +34,9 @@ enum rcs_status {
     RCS_ESIZE = -2,   /* buffer length differs from 8 + 12 n, or an array is too short */
     RCS_EHEADER = -3, /* step file header inconsistent (n <= 0, step < 0, n mismatch) */
     RCS_EHIP = -4,    /* a HIP launch, copy or allocation failed */
-    RCS_ENOMEM = -5   /* workspace allocation failed */
+    RCS_ENOMEM = -5,  /* workspace allocation failed */
+    RCS_EIO = -6,     /* a file could not be written, read or renamed */
+    RCS_ENOENT = -7   /* no such file, or no valid step file in the directory */
 };
 
 /* Largest n the step file's int32 header can describe. */
@@ -86,6 +88,19 @@ int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int
                     float lr, float wd, float clip, hipStream_t stream);
 
 /*
+ * adamw_clip_step for a gradient accumulated over micro-batches: g holds the
+ * sum of n_micro micro-batch gradients (backward passes add into one buffer)
+ * and grad_scale = 1/n_micro. Each element is first multiplied by grad_scale
+ * in float32 (the averaging step the backprop lesson runs before the optimizer
+ * step, under "accumulation over micro-batches"), then norm, clip and update
+ * proceed exactly as in adamw_clip_step on that averaged gradient. The scale
+ * is applied in registers in both kernels; g is not written. grad_scale must
+ * be finite and > 0; adamw_clip_step is this call with grad_scale = 1.
+ */
+int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
+                          float lr, float wd, float clip, float grad_scale, hipStream_t stream);
+
+/*
  * The pre-clip global norm alone: sqrt(sum_i (double)g[i]^2), same kernels and
  * order as adamw_clip_step. norm_out is device memory or pinned host memory
  * and receives one float64 once the stream reaches this call.
@@ -130,6 +145,69 @@ int ckpt_pack(int32_t step, int64_t n, const float *w, const float *m, const flo
  */
 int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int32_t *step_out,
                 float *w, float *m, float *v, hipStream_t stream);
+
+/*
+ * Asynchronous pack, so the training stream does not stall for the host
+ * link (the sharded-resume lesson's "async write" production pattern):
+ *   1. on compute_stream, in order after the updates already enqueued there,
+ *      a kernel copies w, m, v into `snapshot` (device float32[3n], the file
+ *      payload [w | m | v]): 24 B per parameter at HBM speed;
+ *   2. copy_stream waits for that kernel, then copies the snapshot to
+ *      host_buf + 8; the header is written by the host before returning.
+ * Updates enqueued on compute_stream afterwards may change w, m, v at once;
+ * the packed bytes are those of the state at the call. A later
+ * ckpt_pack_async on the same snapshot makes compute_stream wait until the
+ * earlier copy out of it has finished. host_buf must not be read or reused
+ * until ckpt_pack_wait(snapshot) returns (or copy_stream is synchronized).
+ * Sizes: snapshot_bytes == ckpt_snapshot_bytes(n) == 12 n, buf_bytes ==
+ * ckpt_bytes(n). The snapshot must not overlap w, m or v.
+ */
+int64_t ckpt_snapshot_bytes(int64_t n);
+int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, const float *v,
+                    float *snapshot, int64_t snapshot_bytes, void *host_buf, int64_t buf_bytes,
+                    hipStream_t compute_stream, hipStream_t copy_stream);
+/* Blocks until the last ckpt_pack_async out of `snapshot` has landed in its
+ * host buffer (RCS_OK at once if there is none). */
+int ckpt_pack_wait(const float *snapshot);
+
+/*
+ * On-disk step files (grow_a_language_model_checkpoints, "SIGTERM &
+ * SIGUSR1"; the sharded-resume lesson's atomic write). All host-only; none
+ * touches the device.
+ *
+ * ckpt_file_write: host_buf holds a packed state (as ckpt_pack leaves it,
+ * after its copies have completed); its header must be consistent with
+ * buf_bytes. Writes <dir>/step_%06d.bin.tmp, fsyncs it, renames it to
+ * <dir>/step_%06d.bin (atomic on POSIX) and fsyncs the directory, so a crash
+ * leaves either the old set of files or the new complete file. The final path
+ * is copied to path_out (if not NULL; RCS_EINVAL if path_cap is too small).
+ * ckpt_file_size: size in bytes of a regular file, or RCS_ENOENT.
+ * ckpt_file_read: reads a whole file into host_buf; its size must equal
+ * buf_bytes (RCS_ESIZE) and its header must be consistent (RCS_EHEADER).
+ * ckpt_file_latest: the valid step file with the highest step in dir (name
+ * step_<digits>.bin matching the header's step, header consistent with the
+ * size); temporaries and malformed files are skipped; RCS_ENOENT if none.
+ * ckpt_file_rotate: keeps the `keep` newest valid step files, deletes the
+ * older ones and any step_*.bin.tmp leftovers; returns how many were removed.
+ */
+int ckpt_file_write(const char *dir, const void *host_buf, int64_t buf_bytes, char *path_out,
+                    int64_t path_cap);
+int64_t ckpt_file_size(const char *path);
+int ckpt_file_read(const char *path, void *host_buf, int64_t buf_bytes);
+int ckpt_file_latest(const char *dir, int32_t *step_out, char *path_out, int64_t path_cap);
+int ckpt_file_rotate(const char *dir, int keep);
+
+/*
+ * SIGTERM / SIGUSR1 (grow_a_language_model_checkpoints, "SIGTERM & SIGUSR1"):
+ * rcs_signals_install sets handlers that only raise flags; the training loop
+ * calls rcs_signals_poll after each completed update and gets a bit mask
+ * (cleared by the call): RCS_SIG_WRITE_CONTINUE (SIGUSR1: write the step file
+ * and carry on), RCS_SIG_WRITE_EXIT (SIGTERM: write the step file and exit).
+ */
+#define RCS_SIG_WRITE_CONTINUE 1
+#define RCS_SIG_WRITE_EXIT 2
+int rcs_signals_install(void);
+int rcs_signals_poll(void);
 
 /*
  * Instrumentation: while enabled, adamw_clip_step records HIP events on its

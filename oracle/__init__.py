@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_ckpt_header.restype = ctypes.c_int
         L.oracle_ckpt_unpack.argtypes = [u8p, i64, i64, ctypes.POINTER(i32), f32p, f32p, f32p]
         L.oracle_ckpt_unpack.restype = ctypes.c_int
+        L.oracle_scale_grads.argtypes = [f32p, i64, ctypes.c_float]
+        L.oracle_scale_grads.restype = None
         L.oracle_subnormals_kept.argtypes = []
         L.oracle_subnormals_kept.restype = ctypes.c_int
         _lib = L
@@ -147,6 +149,20 @@ def adamw_clip_step(w, g, m, v, t: int, lr: float, wd: float, clip: float):
     rc = lib().oracle_adamw_clip_step(_f32(w, True), _f32(g), _f32(m, True), _f32(v, True), n,
                                       t, lr, wd, clip, ctypes.byref(norm))
     return rc, norm.value
+
+
+def scale_grads(g: np.ndarray, scale: float) -> None:
+    """In place: g *= scale in float32 (micro-batch averaging)."""
+    lib().oracle_scale_grads(_f32(g, True), g.size, scale)
+
+
+def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: float,
+                          grad_scale: float):
+    """The pages' order: average the accumulated gradient (g *= grad_scale,
+    float32), then the clipped update. g_sum is left untouched."""
+    g = g_sum.copy()
+    scale_grads(g, grad_scale)
+    return adamw_clip_step(w, g, m, v, t, lr, wd, clip)
 
 
 def scalar_step_f64(state, g: float, lr: float, wd: float, clip: float):

@@ -130,6 +130,14 @@ void oracle_adamw_elems(float *w, const float *g, float *m, float *v, int64_t n,
     }
 }
 
+/* The averaging step of gradient accumulation, grow_a_language_model_backprop,
+ * section on accumulation over micro-batches: backward passes add into one
+ * gradient buffer, then every element is multiplied by 1/n_micro (a float32
+ * multiply) before the optimizer step. */
+void oracle_scale_grads(float *g, int64_t n, float scale) {
+    for (int64_t i = 0; i < n; ++i) g[i] = g[i] * scale;
+}
+
 /* One full update: norm, clip factor, scalars, elementwise step.
  * Returns ORACLE_OK, ORACLE_SKIPPED (non-finite norm, R3) or ORACLE_EINVAL. */
 int oracle_adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,

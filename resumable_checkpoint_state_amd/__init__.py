@@ -24,7 +24,8 @@ __all__ = [
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
 ]
 
-OK, EINVAL, ESIZE, EHEADER, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ESIZE, EHEADER, EHIP, ENOMEM, EIO, ENOENT = 0, -1, -2, -3, -4, -5, -6, -7
+SIG_WRITE_CONTINUE, SIG_WRITE_EXIT = 1, 2
 MAX_N = 2_147_483_647
 
 
@@ -71,6 +72,29 @@ def lib() -> ctypes.CDLL:
     L.rcs_profile_read.restype = ctypes.c_int
     L.rcs_fp32_div_sqrt_probe.argtypes = [f32p, f32p, f32p, f32p, i64, vp]
     L.rcs_fp32_div_sqrt_probe.restype = ctypes.c_int
+    L.adamw_clip_step_accum.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, f32, vp]
+    L.adamw_clip_step_accum.restype = ctypes.c_int
+    L.ckpt_snapshot_bytes.argtypes = [i64]
+    L.ckpt_snapshot_bytes.restype = i64
+    L.ckpt_pack_async.argtypes = [i32, i64, f32p, f32p, f32p, f32p, i64, vp, i64, vp, vp]
+    L.ckpt_pack_async.restype = ctypes.c_int
+    L.ckpt_pack_wait.argtypes = [f32p]
+    L.ckpt_pack_wait.restype = ctypes.c_int
+    cp = ctypes.c_char_p
+    L.ckpt_file_write.argtypes = [cp, vp, i64, ctypes.c_char_p, i64]
+    L.ckpt_file_write.restype = ctypes.c_int
+    L.ckpt_file_size.argtypes = [cp]
+    L.ckpt_file_size.restype = i64
+    L.ckpt_file_read.argtypes = [cp, vp, i64]
+    L.ckpt_file_read.restype = ctypes.c_int
+    L.ckpt_file_latest.argtypes = [cp, ctypes.POINTER(i32), ctypes.c_char_p, i64]
+    L.ckpt_file_latest.restype = ctypes.c_int
+    L.ckpt_file_rotate.argtypes = [cp, ctypes.c_int]
+    L.ckpt_file_rotate.restype = ctypes.c_int
+    L.rcs_signals_install.argtypes = []
+    L.rcs_signals_install.restype = ctypes.c_int
+    L.rcs_signals_poll.argtypes = []
+    L.rcs_signals_poll.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -115,6 +139,18 @@ def adamw_clip_step(w, g, m, v, t: int, lr: float, wd: float, clip: float, strea
     args = (_dev_f32(w, "w"), _dev_f32(g, "g", n), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
     _check(lib().adamw_clip_step(*args, n, int(t), float(lr), float(wd), float(clip),
                                  _stream(stream)), "adamw_clip_step")
+
+
+def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: float,
+                          grad_scale: float, stream=None) -> None:
+    """The update for a gradient summed over micro-batches: each element of
+    g_sum is multiplied by the float32 grad_scale (1/n_micro) inside the
+    kernels before norm, clip and update; g_sum is not written."""
+    n = w.numel()
+    args = (_dev_f32(w, "w"), _dev_f32(g_sum, "g", n), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    _check(lib().adamw_clip_step_accum(*args, n, int(t), float(lr), float(wd), float(clip),
+                                       float(grad_scale), _stream(stream)),
+           "adamw_clip_step_accum")
 
 
 def _norm_out(out):
@@ -176,6 +212,117 @@ def ckpt_unpack(buf: torch.Tensor, w, m, v, stream=None) -> int:
     _check(lib().ckpt_unpack(_host_u8(buf, "buf"), buf.numel(), n, ctypes.byref(step), *ptrs,
                              _stream(stream)), "ckpt_unpack")
     return step.value
+
+
+def ckpt_snapshot_bytes(n: int) -> int:
+    return lib().ckpt_snapshot_bytes(n)
+
+
+def ckpt_pack_async(step: int, w, m, v, snapshot, buf: torch.Tensor, compute_stream=None,
+                    copy_stream=None) -> torch.Tensor:
+    """Snapshot w, m, v on the compute stream, drain to buf on the copy stream;
+    call ckpt_pack_wait(snapshot) before reading buf."""
+    n = w.numel()
+    ptrs = (_dev_f32(w, "w"), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    sp = _dev_f32(snapshot, "snapshot", 3 * n)
+    if copy_stream is None:
+        raise ValueError("ckpt_pack_async needs a separate copy stream")
+    _check(lib().ckpt_pack_async(int(step), n, *ptrs, sp, 4 * snapshot.numel(),
+                                 _host_u8(buf, "buf"), buf.numel(), _stream(compute_stream),
+                                 _stream(copy_stream)), "ckpt_pack_async")
+    return buf
+
+
+def ckpt_pack_wait(snapshot) -> None:
+    _check(lib().ckpt_pack_wait(_dev_f32(snapshot, "snapshot")), "ckpt_pack_wait")
+
+
+def _b(path) -> bytes:
+    return os.fsencode(path)
+
+
+def ckpt_file_write(directory, buf: torch.Tensor) -> str:
+    """Atomically writes a packed state (copies complete) as <dir>/step_NNNNNN.bin."""
+    out = ctypes.create_string_buffer(4096)
+    _check(lib().ckpt_file_write(_b(directory), _host_u8(buf, "buf"), buf.numel(), out, 4096),
+           "ckpt_file_write")
+    return os.fsdecode(out.value)
+
+
+def ckpt_file_read(path, buf: torch.Tensor | None = None, pin: bool = True) -> torch.Tensor:
+    size = lib().ckpt_file_size(_b(path))
+    _check(int(size) if size < 0 else 0, "ckpt_file_size")
+    if buf is None:
+        buf = torch.empty(size, dtype=torch.uint8, pin_memory=pin)
+    _check(lib().ckpt_file_read(_b(path), _host_u8(buf, "buf"), buf.numel()), "ckpt_file_read")
+    return buf
+
+
+def ckpt_file_latest(directory):
+    """(step, path) of the newest valid step file, or None."""
+    step = ctypes.c_int32(-1)
+    out = ctypes.create_string_buffer(4096)
+    rc = lib().ckpt_file_latest(_b(directory), ctypes.byref(step), out, 4096)
+    if rc == ENOENT:
+        return None
+    _check(rc, "ckpt_file_latest")
+    return step.value, os.fsdecode(out.value)
+
+
+def ckpt_file_rotate(directory, keep: int) -> int:
+    return _check(lib().ckpt_file_rotate(_b(directory), int(keep)), "ckpt_file_rotate")
+
+
+def signals_install() -> None:
+    _check(lib().rcs_signals_install(), "rcs_signals_install")
+
+
+def signals_poll() -> int:
+    return lib().rcs_signals_poll()
+
+
+class StepFileCheckpointer:
+    """Step-file policy around a training loop: call after_step(t, w, m, v)
+    after every completed update. It writes <dir>/step_NNNNNN.bin when t is a
+    multiple of `every`, when SIGUSR1 arrived (write and continue) or when
+    SIGTERM arrived (write, then after_step returns True: the caller exits),
+    keeps the newest `keep` files, and resume() loads the newest valid one."""
+
+    def __init__(self, directory, n: int, every: int = 100, keep: int = 3,
+                 install_signals: bool = True, stream=None):
+        self.dir, self.n, self.every, self.keep = directory, int(n), int(every), int(keep)
+        os.makedirs(directory, exist_ok=True)
+        self.buf = torch.empty(ckpt_bytes(self.n), dtype=torch.uint8, pin_memory=True)
+        self.stream = stream
+        self.written: list[str] = []
+        if install_signals:
+            signals_install()
+
+    def save(self, t: int, w, m, v) -> str:
+        ckpt_pack(t, w, m, v, self.buf, stream=self.stream)
+        torch.cuda.synchronize()
+        path = ckpt_file_write(self.dir, self.buf)
+        self.written.append(path)
+        ckpt_file_rotate(self.dir, self.keep)
+        return path
+
+    def after_step(self, t: int, w, m, v) -> bool:
+        sig = signals_poll()
+        if sig or (self.every > 0 and t % self.every == 0):
+            self.save(t, w, m, v)
+        return bool(sig & SIG_WRITE_EXIT)
+
+    def resume(self, w, m, v) -> int:
+        """Loads the newest valid step file into w, m, v; returns its step
+        (0 when there is none: a fresh run). Continue with t = step + 1."""
+        found = ckpt_file_latest(self.dir)
+        if found is None:
+            return 0
+        _, path = found
+        ckpt_file_read(path, self.buf)
+        step = ckpt_unpack(self.buf, w, m, v, stream=self.stream)
+        torch.cuda.synchronize()
+        return step
 
 
 def profile_enable(on: bool, max_records: int = 4096, every: int = 1) -> None:

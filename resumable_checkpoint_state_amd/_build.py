@@ -7,6 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "rcs.hip")
+SRC_IO = os.path.join(PKG, "csrc", "ckpt_io.cpp")
 LIB = os.path.join(PKG, "librcs.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -30,7 +31,7 @@ def hipcc() -> str:
 def build(extra_flags: list[str] | None = None, out: str | None = None) -> str:
     out = out or LIB
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, SRC_IO, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

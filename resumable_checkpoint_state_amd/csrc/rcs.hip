@@ -93,6 +93,7 @@ struct ClipScalars {
 
 struct StepScalars {
     float lr, bc1, bc2, decay;
+    float gscale;  // micro-batch averaging factor applied to g first (1 = none)
 };
 
 // ---------------------------------------------------------------- reductions
@@ -138,8 +139,10 @@ __device__ __forceinline__ double block_sum(double x, double *lds) {
     return r;
 }
 
-__device__ __forceinline__ double sq(float x) {
-    const double d = (double)x;
+// Square, in float64, of the gradient after the float32 micro-batch scale
+// (x * gscale is one float32 rounding; gscale = 1 leaves x unchanged).
+__device__ __forceinline__ double sq(float x, float gscale) {
+    const double d = (double)(x * gscale);
     return d * d;
 }
 
@@ -147,7 +150,7 @@ __device__ __forceinline__ double sq(float x) {
 // are read with streaming loads, the rest with cache-allocating loads.
 __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *__restrict__ g,
                                                                   int64_t n, int vec_ok,
-                                                                  int64_t nt_limit4,
+                                                                  int64_t nt_limit4, float gscale,
                                                                   double *__restrict__ partials) {
     __shared__ double lds[kNormThreads / kWave];
     double acc[kNormUnroll];
@@ -174,18 +177,18 @@ __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *_
             }
 #pragma unroll
             for (int j = 0; j < kNormUnroll; ++j) {
-                acc[j] += sq(x[j].x);
-                acc[j] += sq(x[j].y);
-                acc[j] += sq(x[j].z);
-                acc[j] += sq(x[j].w);
+                acc[j] += sq(x[j].x, gscale);
+                acc[j] += sq(x[j].y, gscale);
+                acc[j] += sq(x[j].z, gscale);
+                acc[j] += sq(x[j].w, gscale);
             }
         }
         const int rem = (int)(n & 3);
-        if (blockIdx.x == 0 && (int)threadIdx.x < rem) acc[0] += sq(g[(n4 << 2) + threadIdx.x]);
+        if (blockIdx.x == 0 && (int)threadIdx.x < rem) acc[0] += sq(g[(n4 << 2) + threadIdx.x], gscale);
     } else {
         for (int64_t i = (int64_t)blockIdx.x * kNormThreads + threadIdx.x; i < n;
              i += nblk * kNormThreads)
-            acc[0] += sq(g[i]);
+            acc[0] += sq(g[i], gscale);
     }
     const double t = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     const double b = block_sum<kNormThreads>(t, lds);
@@ -219,7 +222,8 @@ __global__ __launch_bounds__(kFinalThreads) void grad_norm_final(const double *_
 // The float32 op sequence of one element; every line is one rounding.
 __device__ __forceinline__ void adamw_elem(float &w, float g, float &m, float &v, float s,
                                            const StepScalars &h) {
-    const float gp = g * s;
+    const float ga = g * h.gscale;
+    const float gp = ga * s;
     const float mi = 0.9f * m + 0.1f * gp;
     const float vi = 0.999f * v + 0.001f * (gp * gp);
     const float mh = mi / h.bc1;
@@ -334,6 +338,35 @@ __global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restri
     }
 }
 
+// a4 (asynchronous form): copy w, m, v into one device snapshot laid out like
+// the step file's payload [w | m | v], so that the training stream can keep
+// updating w, m, v while the snapshot drains to the host on a copy stream.
+// Vector path: n % 4 == 0 and all pointers 16-byte aligned; lane i copies
+// snapshot vector i, taken from w, m or v by which third it falls in.
+__global__ __launch_bounds__(256) void ckpt_snapshot_vec(const f32x4 *__restrict__ w,
+                                                         const f32x4 *__restrict__ m,
+                                                         const f32x4 *__restrict__ v,
+                                                         f32x4 *__restrict__ snap, int64_t n4) {
+    const int64_t total = 3 * n4;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const f32x4 *src = (i < n4) ? w + i : (i < 2 * n4) ? m + (i - n4) : v + (i - 2 * n4);
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src), snap + i);
+    }
+}
+
+__global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restrict__ w,
+                                                            const float *__restrict__ m,
+                                                            const float *__restrict__ v,
+                                                            float *__restrict__ snap, int64_t n) {
+    const int64_t total = 3 * n;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+        const float *src = (i < n) ? w + i : (i < 2 * n) ? m + (i - n) : v + (i - 2 * n);
+        snap[i] = *src;
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 struct Workspace {
@@ -344,6 +377,15 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Per snapshot buffer: `ready` is recorded on the compute stream after the
+// snapshot kernel, `copied` on the copy stream after the device-to-host copy.
+struct SnapshotSync {
+    hipEvent_t ready = nullptr;
+    hipEvent_t copied = nullptr;
+    bool pending = false;  // a copy out of this snapshot has been enqueued
+};
+std::map<std::pair<int, const void *>, SnapshotSync> g_snap;
 
 struct Profile {
     bool on = false;
@@ -422,10 +464,11 @@ int64_t norm_nt_limit4(int64_t n) {
     return n4 > tail4 ? n4 - tail4 : 0;
 }
 
-int launch_norm(const float *g, int64_t n, float clip, Workspace *ws, hipStream_t stream) {
+int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *ws,
+                hipStream_t stream) {
     const int nb = norm_blocks(n);
     hipLaunchKernelGGL(grad_norm_partial, dim3(nb), dim3(kNormThreads), 0, stream, g, n,
-                       aligned16(g) ? 1 : 0, norm_nt_limit4(n), ws->partials);
+                       aligned16(g) ? 1 : 0, norm_nt_limit4(n), gscale, ws->partials);
     hipLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream,
                        (const double *)ws->partials, nb, clip, ws->scalars);
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
@@ -476,6 +519,8 @@ const char *rcs_strerror(int status) {
         case RCS_EHEADER: return "step file header rejected (n <= 0, step < 0 or n differs from the expected n)";
         case RCS_EHIP: return "HIP launch, copy or allocation failed";
         case RCS_ENOMEM: return "workspace allocation failed";
+        case RCS_EIO: return "file write, read or rename failed";
+        case RCS_ENOENT: return "no such file, or no valid step file in the directory";
         default: return "unknown status";
     }
 }
@@ -495,7 +540,13 @@ int rcs_init(int device, hipStream_t stream) {
 
 int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t, float lr,
                     float wd, float clip, hipStream_t stream) {
+    return adamw_clip_step_accum(w, g, m, v, n, t, lr, wd, clip, 1.0f, stream);
+}
+
+int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
+                          float lr, float wd, float clip, float grad_scale, hipStream_t stream) {
     if (!valid_n(n) || t < 1) return RCS_EINVAL;
+    if (!std::isfinite(grad_scale) || !(grad_scale > 0.0f)) return RCS_EINVAL;
     if (!std::isfinite(lr) || !std::isfinite(wd) || std::isnan(clip) || !(clip > 0.0f))
         return RCS_EINVAL;
     const int64_t bytes = 4 * n;
@@ -516,6 +567,7 @@ int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int
     h.bc1 = (float)(1.0 - std::pow(0.9, (double)t));
     h.bc2 = (float)(1.0 - std::pow(0.999, (double)t));
     h.decay = (float)(1.0 - (double)lr * (double)wd);
+    h.gscale = grad_scale;
 
     hipEvent_t *ev = nullptr;
     {
@@ -524,7 +576,7 @@ int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int
             ev = &g_prof.ev[3 * g_prof.next++];
     }
     if (ev) (void)hipEventRecord(ev[0], stream);
-    if ((rc = launch_norm(g, n, clip, ws, stream)) != RCS_OK) return rc;
+    if ((rc = launch_norm(g, n, grad_scale, clip, ws, stream)) != RCS_OK) return rc;
     if (ev) (void)hipEventRecord(ev[1], stream);
     rc = launch_update(w, g, m, v, n, ws->scalars, h, stream);
     if (ev) (void)hipEventRecord(ev[2], stream);
@@ -538,7 +590,7 @@ int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t st
     if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
     Workspace *ws = nullptr;
     if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
-    if ((rc = launch_norm(g, n, INFINITY, ws, stream)) != RCS_OK) return rc;
+    if ((rc = launch_norm(g, n, 1.0f, INFINITY, ws, stream)) != RCS_OK) return rc;
     ws->has_norm = true;
     if (hipMemcpyAsync(norm_out, &ws->scalars->norm, sizeof(double), hipMemcpyDefault, stream) !=
         hipSuccess)
@@ -600,6 +652,84 @@ int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int
         return RCS_EHIP;
     *step_out = step;
     return RCS_OK;
+}
+
+int64_t ckpt_snapshot_bytes(int64_t n) { return valid_n(n) ? 12 * n : -1; }
+
+int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, const float *v,
+                    float *snapshot, int64_t snapshot_bytes, void *host_buf, int64_t buf_bytes,
+                    hipStream_t compute_stream, hipStream_t copy_stream) {
+    if (!valid_n(n) || step < 0 || host_buf == nullptr) return RCS_EINVAL;
+    if (buf_bytes != ckpt_bytes(n) || snapshot_bytes != 12 * n) return RCS_ESIZE;
+    const int64_t bytes = 4 * n;
+    int rc;
+    if ((rc = check_device_range(w, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(snapshot, 3 * bytes)) != RCS_OK) return rc;
+    if (overlaps(snapshot, w, 3 * bytes) || overlaps(snapshot, m, 3 * bytes) ||
+        overlaps(snapshot, v, 3 * bytes) || overlaps(w, snapshot, bytes) ||
+        overlaps(m, snapshot, bytes) || overlaps(v, snapshot, bytes))
+        return RCS_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
+    SnapshotSync *ss = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        SnapshotSync &e = g_snap[std::make_pair(dev, (const void *)snapshot)];
+        if (e.ready == nullptr) {
+            if (hipEventCreateWithFlags(&e.ready, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&e.copied, hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                return RCS_EHIP;
+            }
+        }
+        ss = &e;
+    }
+    // the snapshot must not be overwritten while an earlier copy still reads it
+    if (ss->pending && hipStreamWaitEvent(compute_stream, ss->copied, 0) != hipSuccess)
+        return RCS_EHIP;
+    if (n % 4 == 0 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(snapshot)) {
+        const int64_t total = 3 * (n >> 2);
+        int64_t blocks = (total + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(ckpt_snapshot_vec, dim3((unsigned)blocks), dim3(256), 0, compute_stream,
+                           reinterpret_cast<const f32x4 *>(w), reinterpret_cast<const f32x4 *>(m),
+                           reinterpret_cast<const f32x4 *>(v), reinterpret_cast<f32x4 *>(snapshot),
+                           n >> 2);
+    } else {
+        int64_t blocks = (3 * n + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(ckpt_snapshot_scalar, dim3((unsigned)blocks), dim3(256), 0,
+                           compute_stream, w, m, v, snapshot, n);
+    }
+    if (hipGetLastError() != hipSuccess) return RCS_EHIP;
+    if (hipEventRecord(ss->ready, compute_stream) != hipSuccess ||
+        hipStreamWaitEvent(copy_stream, ss->ready, 0) != hipSuccess)
+        return RCS_EHIP;
+    unsigned char *b = static_cast<unsigned char *>(host_buf);
+    put_le32(b, step);
+    put_le32(b + 4, (int32_t)n);
+    if (hipMemcpyAsync(b + 8, snapshot, 3 * bytes, hipMemcpyDeviceToHost, copy_stream) !=
+            hipSuccess ||
+        hipEventRecord(ss->copied, copy_stream) != hipSuccess)
+        return RCS_EHIP;
+    ss->pending = true;
+    return RCS_OK;
+}
+
+int ckpt_pack_wait(const float *snapshot) {
+    if (snapshot == nullptr) return RCS_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
+    hipEvent_t e = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_snap.find(std::make_pair(dev, (const void *)snapshot));
+        if (it == g_snap.end() || !it->second.pending) return RCS_OK;
+        e = it->second.copied;
+    }
+    return hipEventSynchronize(e) == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
 int rcs_profile_enable(int on, int max_records, int every) {

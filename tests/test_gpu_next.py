@@ -1,0 +1,143 @@
+"""GPU tests of the rows built on top of the hot path: micro-batch
+accumulation folded into the kernels, the asynchronous snapshot pack, and
+signal-driven step files with resume."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import resumable_checkpoint_state_amd as rcs
+import workloads
+from util import bits, max_ulp
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rcs.lib()
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("n_micro", [1, 3, 4])
+def test_accumulated_microbatch_step_parity(dev, n_micro):
+    wl = workloads.WORKLOADS["andrea12m"]
+    n = 1_000_003
+    w = workloads.init_params(wl, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    scale = float(np.float32(1.0) / np.float32(n_micro))
+    for t in (1, 2, 3):
+        g_sum = torch.zeros(n, device=dev)
+        for k in range(n_micro):  # backward passes add into one buffer
+            g_sum.add_(workloads.custom(200 + 10 * t + k, n, 0.05, device=dev))
+        rcs.adamw_clip_step_accum(w, g_sum, m, v, t, wl.lr, wl.wd, wl.clip, scale)
+        gn = float(rcs.last_grad_norm().cpu())
+        rc, on = oracle.adamw_clip_step_accum(ow, _host(g_sum), om, ov, t, wl.lr, wl.wd, wl.clip,
+                                              scale)
+        assert rc == oracle.OK and on > wl.clip
+        assert abs(gn - on) <= 1e-12 * on
+        for name, a, b in (("w", w, ow), ("m", m, om), ("v", v, ov)):
+            assert max_ulp(_host(a), b) <= 2, (n_micro, t, name)
+
+
+def test_accum_with_unit_scale_equals_plain_step(dev):
+    n = 100_000
+    wl = workloads.WORKLOADS["flat262k"]
+    g = workloads.grads(wl, 1, device=dev, n=n).mul_(40)
+    a = [workloads.init_params(wl, device=dev, n=n), *workloads.zeros_like_state(n, device=dev)]
+    b = [x.clone() for x in a]
+    rcs.adamw_clip_step(a[0], g, a[1], a[2], 1, wl.lr, wl.wd, wl.clip)
+    rcs.adamw_clip_step_accum(b[0], g, b[1], b[2], 1, wl.lr, wl.wd, wl.clip, 1.0)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.parametrize("n", [262_147, 12_800_000])
+def test_async_pack_equals_synchronous_pack_while_training_continues(dev, n):
+    """Snapshot at step k, keep updating on the compute stream while the copy
+    stream drains; the bytes are the state at k. A second async pack out of
+    the same snapshot buffer two steps later is ordered after the first copy."""
+    wl = workloads.WORKLOADS["flat262k"]
+    k = 5
+    w = workloads.init_params(wl, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ref = [w.clone(), m.clone(), v.clone()]
+    g = torch.empty(n, device=dev)
+    nb = rcs.ckpt_bytes(n)
+    ref_bufs = {}
+    for t in range(1, k + 3):  # reference: synchronous packs at k and k + 2
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(ref[0], g, ref[1], ref[2], t, wl.lr, wl.wd, wl.clip)
+        if t in (k, k + 2):
+            ref_bufs[t] = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+            rcs.ckpt_pack(t, *ref, ref_bufs[t])
+    torch.cuda.synchronize()
+    snap = torch.empty(rcs.ckpt_snapshot_bytes(n) // 4, device=dev)
+    copy_stream = torch.cuda.Stream()
+    bufs = {t: torch.empty(nb, dtype=torch.uint8, pin_memory=True) for t in (k, k + 2)}
+    compute = torch.cuda.current_stream()
+    for t in range(1, k + 12):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        if t in (k, k + 2):
+            rcs.ckpt_pack_async(t, w, m, v, snap, bufs[t], compute_stream=compute,
+                                copy_stream=copy_stream)
+    rcs.ckpt_pack_wait(snap)
+    torch.cuda.synchronize()
+    for t in (k, k + 2):
+        assert torch.equal(bufs[t], ref_bufs[t]), f"async pack at step {t} differs"
+    # and the layout is the oracle's: repacking the arrays read out of it gives the same bytes
+    _, ob = oracle.ckpt_pack(k, *[a.numpy() for a in _unpacked(bufs[k], n)])
+    assert ob.tobytes() == bufs[k].numpy().tobytes()
+
+
+def _unpacked(buf, n):
+    raw = buf.numpy()
+    return [torch.from_numpy(raw[8 + 4 * j * n: 8 + 4 * (j + 1) * n].view(np.float32).copy())
+            for j in range(3)]
+
+
+def test_signal_driven_step_files_resume_bit_identical(dev, tmp_path):
+    """A child trains, gets SIGUSR1 after step 30 (writes, continues) and
+    SIGTERM after step 70 (writes, exits); a second child resumes from the
+    newest file and finishes 100 steps. Its final state equals a straight run
+    byte for byte."""
+    wl, n, total = "flat262k", 262_144, 100
+    env = dict(os.environ)
+    cmd = [sys.executable, "-u", os.path.join(HERE, "resume_child.py"), str(tmp_path), wl,
+           str(n), str(total)]
+    r1 = subprocess.run(cmd + ["30", "70"], capture_output=True, text=True, timeout=240, env=env)
+    print(r1.stdout, r1.stderr[-2000:])
+    assert r1.returncode == 0
+    assert "SIGTERM after step 70" in r1.stdout
+    names = sorted(os.listdir(tmp_path))
+    assert names == ["step_000030.bin", "step_000070.bin"], names
+    r2 = subprocess.run(cmd + ["0", "0"], capture_output=True, text=True, timeout=240, env=env)
+    print(r2.stdout, r2.stderr[-2000:])
+    assert r2.returncode == 0 and "resumed at step 70" in r2.stdout
+    final = open(tmp_path / "step_000100.bin", "rb").read()
+    # straight run in this process
+    W = workloads.WORKLOADS[wl]
+    w = workloads.init_params(W, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    g = torch.empty(n, device=dev)
+    for t in range(1, total + 1):
+        workloads.grads(W, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, W.lr, W.wd, W.clip)
+    buf = torch.empty(rcs.ckpt_bytes(n), dtype=torch.uint8, pin_memory=True)
+    rcs.ckpt_pack(total, w, m, v, buf)
+    torch.cuda.synchronize()
+    assert buf.numpy().tobytes() == final

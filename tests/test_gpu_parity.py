@@ -325,3 +325,60 @@ def test_resume_bit_identical_stress_full_size(dev):
     wl = workloads.WORKLOADS["andrea120m_stress"]
     _, _, _, packed = _straight_vs_resumed(dev, wl, wl.steps, 100)
     assert packed.numel() == 1_492_282_376
+
+
+# ---------------------------------------------------------------- near the int32 limit
+
+@pytest.mark.timeout(600)
+def test_flat2e9_sampled_parity_and_pack(dev):
+    """n = 2e9 (32 GB of w, g, m, v): two updates in the launch configuration
+    the benchmark times; the float64 norm is checked against the oracle's norm
+    streamed over all 2e9 gradients, w, m, v on 1 Mi-element chunks spread
+    over the vector (the first and the last included), then one 24 GB pack:
+    header and sampled byte ranges, and an unpack that restores w, m, v bit
+    for bit."""
+    wl = workloads.WORKLOADS["flat2e9"]
+    n = wl.n
+    chunk = 1 << 20
+    offs = sorted({0, n - chunk, *[int(k * (n - chunk) // 13) for k in range(1, 13)]})
+    print(f"flat2e9: n={n}, {len(offs)} sampled chunks", flush=True)
+    w = workloads.init_params(wl, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    g = torch.empty(n, device=dev)
+    workloads.grads(wl, 1, device=dev, out=g)
+    rcs.adamw_clip_step(w, g, m, v, 1, wl.lr, wl.wd, wl.clip)
+    workloads.grads(wl, 2, device=dev, out=g)
+    before = {o: [_host(x[o:o + chunk]).copy() for x in (w, g, m, v)] for o in offs}
+    rcs.adamw_clip_step(w, g, m, v, 2, wl.lr, wl.wd, wl.clip)
+    gpu_norm = _gpu_norm()
+    acc = oracle.NormAccumulator()
+    step = 1 << 28
+    for lo in range(0, n, step):
+        acc.add(_host(g[lo:min(lo + step, n)]))
+    onorm = acc.norm()
+    print(f"flat2e9: norm gpu {gpu_norm!r} oracle {onorm!r}", flush=True)
+    assert abs(gpu_norm - onorm) <= NORM_RTOL * onorm
+    s = oracle.clip_scale(onorm, wl.clip)
+    bc1, bc2, decay = oracle.scalars(2, wl.lr, wl.wd)
+    for o in offs:
+        ow, og, om, ov = before[o]
+        oracle.adamw_elems(ow, og, om, ov, float(s), float(bc1), float(bc2), float(decay), wl.lr)
+        _check_state(w[o:o + chunk], m[o:o + chunk], v[o:o + chunk], ow, om, ov,
+                     f"flat2e9 chunk at {o}")
+    del g
+    nb = rcs.ckpt_bytes(n)
+    assert nb == 24_000_000_008
+    buf = _pinned(nb)
+    rcs.ckpt_pack(2, w, m, v, buf)
+    torch.cuda.synchronize()
+    raw = buf.numpy()
+    assert oracle.ckpt_header(raw[:8].copy()) == (oracle.OK, 2, n)
+    for o in (offs[0], offs[len(offs) // 2], offs[-1]):
+        for k, x in enumerate((w, m, v)):
+            lo = 8 + 4 * k * n + 4 * o
+            assert raw[lo:lo + 4 * chunk].tobytes() == _host(x[o:o + chunk]).tobytes()
+    w2, m2, v2 = (torch.empty(n, device=dev) for _ in range(3))
+    assert rcs.ckpt_unpack(buf, w2, m2, v2) == 2
+    torch.cuda.synchronize()
+    for a, b in ((w, w2), (m, m2), (v, v2)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))

@@ -418,3 +418,25 @@ def test_straight_equals_pack_resume_small_trajectory():
         oracle.adamw_clip_step(w3, grads[t - 1], m3, v3, t, *hp)
     assert oracle.ckpt_pack(10, w, m, v)[1].tobytes() == \
         oracle.ckpt_pack(10, w3, m3, v3)[1].tobytes()
+
+
+# ---------------------------------------------------------------- micro-batch accumulation
+
+def test_scale_grads_averages_accumulated_microbatches():
+    """Backward passes add into one buffer, then the sum is multiplied by
+    1/n_micro: two identical micro-batches average back to the gradient
+    exactly (g + g = 2g and 2g * 0.5 = g are exact); three come back within
+    one float32 rounding of each step."""
+    g = (np.random.default_rng(31).standard_normal(10_000) * 0.01).astype(np.float32)
+    two = (g + g).astype(np.float32)
+    oracle.scale_grads(two, 0.5)
+    assert (f32bits(two) == f32bits(g)).all()
+    three = ((g + g) + g).astype(np.float32)
+    oracle.scale_grads(three, float(np.float32(1) / np.float32(3)))
+    assert np.abs(three.astype(np.float64) - g) .max() <= 3 * np.spacing(np.abs(g)).max()
+    # the accumulated step equals the plain step on the averaged gradient
+    w1, m1, v1 = np.full(g.size, 0.5, np.float32), np.zeros_like(g), np.zeros_like(g)
+    w2, m2, v2 = w1.copy(), m1.copy(), v1.copy()
+    oracle.adamw_clip_step_accum(w1, (g + g).astype(np.float32), m1, v1, 1, 3e-3, 0.01, 1.0, 0.5)
+    oracle.adamw_clip_step(w2, g, m2, v2, 1, 3e-3, 0.01, 1.0)
+    assert (f32bits(w1) == f32bits(w2)).all() and (f32bits(m1) == f32bits(m2)).all()
