@@ -192,6 +192,12 @@ int ckpt_pack_wait(const float *snapshot);
  */
 int ckpt_file_write(const char *dir, const void *host_buf, int64_t buf_bytes, char *path_out,
                     int64_t path_cap);
+/* Same atomic write (tmp, fsync, rename, fsync dir) of a packed state to an
+ * explicit path, e.g. one rank's shard file of a sharded checkpoint. */
+int ckpt_file_write_path(const char *path, const void *host_buf, int64_t buf_bytes);
+/* Atomic write of arbitrary bytes (a shard manifest, written last so that a
+ * crash never leaves a manifest pointing at missing or partial shards). */
+int rcs_file_write_atomic(const char *path, const void *data, int64_t len);
 int64_t ckpt_file_size(const char *path);
 int ckpt_file_read(const char *path, void *host_buf, int64_t buf_bytes);
 int ckpt_file_latest(const char *dir, int32_t *step_out, char *path_out, int64_t path_cap);

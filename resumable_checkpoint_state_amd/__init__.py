@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
     cp = ctypes.c_char_p
     L.ckpt_file_write.argtypes = [cp, vp, i64, ctypes.c_char_p, i64]
     L.ckpt_file_write.restype = ctypes.c_int
+    L.ckpt_file_write_path.argtypes = [cp, vp, i64]
+    L.ckpt_file_write_path.restype = ctypes.c_int
+    L.rcs_file_write_atomic.argtypes = [cp, vp, i64]
+    L.rcs_file_write_atomic.restype = ctypes.c_int
     L.ckpt_file_size.argtypes = [cp]
     L.ckpt_file_size.restype = i64
     L.ckpt_file_read.argtypes = [cp, vp, i64]

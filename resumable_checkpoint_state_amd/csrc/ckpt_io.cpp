@@ -143,6 +143,32 @@ std::vector<Found> list_valid(const std::string &dir) {
     return out;
 }
 
+// <path>.tmp, fsync, rename to <path>, fsync the directory.
+int atomic_write(const std::string &final_path, const unsigned char *b, int64_t len) {
+    const std::string tmp_path = final_path + ".tmp";
+    const int fd = open(tmp_path.c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
+    if (fd < 0) return RCS_EIO;
+    int rc = write_all(fd, b, len);
+    if (rc == RCS_OK && fsync(fd) != 0) rc = RCS_EIO;
+    if (close(fd) != 0 && rc == RCS_OK) rc = RCS_EIO;
+    if (rc != RCS_OK) {
+        unlink(tmp_path.c_str());
+        return rc;
+    }
+    if (rename(tmp_path.c_str(), final_path.c_str()) != 0) {
+        unlink(tmp_path.c_str());
+        return RCS_EIO;
+    }
+    const size_t slash = final_path.find_last_of('/');
+    const std::string d = slash == std::string::npos ? "." : final_path.substr(0, slash + 1);
+    const int dfd = open(d.c_str(), O_RDONLY | O_DIRECTORY | O_CLOEXEC);
+    if (dfd >= 0) {
+        (void)fsync(dfd);  // make the rename itself durable
+        close(dfd);
+    }
+    return RCS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,28 +180,23 @@ int ckpt_file_write(const char *dir, const void *host_buf, int64_t buf_bytes, ch
     int32_t step = 0, n = 0;
     int rc = check_header(b, buf_bytes, &step, &n);
     if (rc != RCS_OK) return rc;
-    const std::string d = dir;
-    const std::string final_path = d + "/" + step_name(step);
-    const std::string tmp_path = final_path + ".tmp";
-    const int fd = open(tmp_path.c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
-    if (fd < 0) return RCS_EIO;
-    rc = write_all(fd, b, buf_bytes);
-    if (rc == RCS_OK && fsync(fd) != 0) rc = RCS_EIO;
-    if (close(fd) != 0 && rc == RCS_OK) rc = RCS_EIO;
-    if (rc != RCS_OK) {
-        unlink(tmp_path.c_str());
-        return rc;
-    }
-    if (rename(tmp_path.c_str(), final_path.c_str()) != 0) {
-        unlink(tmp_path.c_str());
-        return RCS_EIO;
-    }
-    const int dfd = open(d.c_str(), O_RDONLY | O_DIRECTORY | O_CLOEXEC);
-    if (dfd >= 0) {
-        (void)fsync(dfd);  // make the rename itself durable
-        close(dfd);
-    }
+    const std::string final_path = std::string(dir) + "/" + step_name(step);
+    if ((rc = atomic_write(final_path, b, buf_bytes)) != RCS_OK) return rc;
     return copy_path(final_path, path_out, path_cap);
+}
+
+int ckpt_file_write_path(const char *path, const void *host_buf, int64_t buf_bytes) {
+    if (path == nullptr || host_buf == nullptr) return RCS_EINVAL;
+    const unsigned char *b = static_cast<const unsigned char *>(host_buf);
+    int32_t step = 0, n = 0;
+    const int rc = check_header(b, buf_bytes, &step, &n);
+    if (rc != RCS_OK) return rc;
+    return atomic_write(path, b, buf_bytes);
+}
+
+int rcs_file_write_atomic(const char *path, const void *data, int64_t len) {
+    if (path == nullptr || (data == nullptr && len > 0) || len < 0) return RCS_EINVAL;
+    return atomic_write(path, static_cast<const unsigned char *>(data), len);
 }
 
 int64_t ckpt_file_size(const char *path) {
