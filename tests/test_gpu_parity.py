@@ -382,3 +382,47 @@ def test_flat2e9_sampled_parity_and_pack(dev):
     torch.cuda.synchronize()
     for a, b in ((w, w2), (m, m2), (v, v2)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ---------------------------------------------------------------- whole runs at full size
+
+def _full_run(dev, wl, check_every):
+    n = wl.n
+    w = workloads.init_params(wl, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = torch.empty(n, device=dev)
+    worst = 0
+    for t in range(1, wl.steps + 1):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        gn = _gpu_norm()
+        rc, on = oracle.adamw_clip_step(ow, _host(g), om, ov, t, wl.lr, wl.wd, wl.clip)
+        assert rc == oracle.OK and abs(gn - on) <= NORM_RTOL * on, (t, gn, on)
+        if t % check_every == 0 or t == wl.steps:
+            for name, a, b in (("w", w, ow), ("m", m, om), ("v", v, ov)):
+                d = max_ulp(_host(a), b)
+                worst = max(worst, d)
+                assert d <= ULP_TOL, f"{wl.name} t={t}: {name} max ulp distance {d}"
+            print(f"{wl.name}: step {t} within {worst} ulp", flush=True)
+        if t in wl.pack_at:
+            buf = _pinned(rcs.ckpt_bytes(n))
+            rcs.ckpt_pack(t, w, m, v, buf)
+            torch.cuda.synchronize()
+            assert oracle.ckpt_header(buf.numpy()[:8].copy()) == (oracle.OK, t, n)
+            if worst == 0:  # identical states pack to identical bytes
+                _, ob = oracle.ckpt_pack(t, ow, om, ov)
+                assert buf.numpy().tobytes() == ob.tobytes()
+    return worst
+
+
+@pytest.mark.timeout(300)
+def test_andrea12m_all_200_steps_against_oracle(dev):
+    wl = workloads.WORKLOADS["andrea12m"]
+    print("andrea12m worst ulp:", _full_run(dev, wl, 20))
+
+
+@pytest.mark.timeout(600)
+def test_andrea120m_all_100_steps_against_oracle(dev):
+    wl = workloads.WORKLOADS["andrea120m"]
+    print("andrea120m worst ulp:", _full_run(dev, wl, 25))
