@@ -91,6 +91,16 @@ def async_pack_overlap(rcs, step, stream, w, m, v, buf, n, k=60):
     rcs.ckpt_pack_async(0, w, m, v, snap, buf, compute_stream=stream, copy_stream=copy_stream)
     rcs.ckpt_pack_wait(snap)  # first touch
     torch.cuda.synchronize()
+    # the snapshot kernel alone: the compute stream's share of an async pack
+    snaps = []
+    for _ in range(3):
+        e0.record(stream)
+        rcs.ckpt_pack_async(0, w, m, v, snap, buf, compute_stream=stream,
+                            copy_stream=copy_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        snaps.append(e0.elapsed_time(e1))
+    snap_ms = sorted(snaps)[1]
     e0.record(stream)
     for _ in range(k):
         step()
@@ -107,7 +117,31 @@ def async_pack_overlap(rcs, step, stream, w, m, v, buf, n, k=60):
     both_wall = (time.perf_counter() - t0) * 1e3
     with_pack = e0.elapsed_time(e1)
     return {"async_pack_steps": k, "steps_ms_alone": alone,
-            "steps_ms_with_async_pack": with_pack, "wall_ms_steps_and_pack": both_wall}
+            "steps_ms_with_async_pack": with_pack, "wall_ms_steps_and_pack": both_wall,
+            "snapshot_ms": snap_ms, "snapshot_GBps_24B_per_param": 24 * n / snap_ms / 1e6}
+
+
+def sharded_rate(rcs, w, m, v, world=8):
+    """Save and load of a sharded checkpoint (world simulated ranks): per-rank
+    pack, atomic shard writes with fsync, sha256, manifest; load verifies all
+    hashes before unpacking."""
+    import shutil
+    import tempfile
+
+    from resumable_checkpoint_state_amd import sharded
+
+    d = tempfile.mkdtemp(prefix="rcs_shards_", dir=os.environ.get("TMPDIR", "/tmp"))
+    try:
+        t0 = time.perf_counter()
+        sharded.save_sharded(d, 1, w, m, v, world)
+        t_save = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        sharded.load_sharded(d, world, w, m, v)
+        t_load = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    return {"sharded_world": world, "sharded_save_ms": t_save * 1e3,
+            "sharded_load_ms": t_load * 1e3}
 
 
 def file_write_rate(rcs, buf):
@@ -280,6 +314,7 @@ def main() -> int:
                           "pack_ms": pack_s * 1e3, "unpack_ms": unpack_s * 1e3}
         result["ckpt"].update(async_pack_overlap(rcs, step, stream, w, m, v, buf, n))
         result["ckpt"].update(file_write_rate(rcs, buf))
+        result["ckpt"].update(sharded_rate(rcs, w, m, v))
         del buf
 
     if not args.no_cpu_baseline:

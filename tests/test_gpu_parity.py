@@ -426,3 +426,34 @@ def test_andrea12m_all_200_steps_against_oracle(dev):
 def test_andrea120m_all_100_steps_against_oracle(dev):
     wl = workloads.WORKLOADS["andrea120m"]
     print("andrea120m worst ulp:", _full_run(dev, wl, 25))
+
+
+@pytest.mark.timeout(600)
+def test_max_n_int32_limit_ragged_tail(dev):
+    """n = 2^31 - 1, the largest n the int32 header can hold (n % 4 == 3, so
+    the vector kernels end in a 3-element scalar tail): one update, norm
+    against the oracle's streamed norm, w, m, v on the first, a middle and the
+    last 1 Mi elements."""
+    n = rcs.MAX_N
+    wl = workloads.WORKLOADS["flat2e9"]
+    chunk = 1 << 20
+    offs = [0, (n // 2) // 4 * 4 + 1, n - chunk]
+    w = workloads.custom(300, n, 0.02, device=dev)
+    g = workloads.custom(301, n, 1e-4, device=dev)
+    m = workloads.custom(302, n, 1e-5, device=dev)
+    v = workloads.custom(303, n, 1e-6, device=dev).square_()
+    before = {o: [_host(x[o:o + chunk]).copy() for x in (w, g, m, v)] for o in offs}
+    rcs.adamw_clip_step(w, g, m, v, 7, wl.lr, wl.wd, wl.clip)
+    gpu_norm = _gpu_norm()
+    acc = oracle.NormAccumulator()
+    for lo in range(0, n, 1 << 28):
+        acc.add(_host(g[lo:min(lo + (1 << 28), n)]))
+    onorm = acc.norm()
+    assert abs(gpu_norm - onorm) <= NORM_RTOL * onorm
+    s = oracle.clip_scale(onorm, wl.clip)
+    bc1, bc2, decay = oracle.scalars(7, wl.lr, wl.wd)
+    for o in offs:
+        ow, og, om, ov = before[o]
+        oracle.adamw_elems(ow, og, om, ov, float(s), float(bc1), float(bc2), float(decay), wl.lr)
+        _check_state(w[o:o + chunk], m[o:o + chunk], v[o:o + chunk], ow, om, ov,
+                     f"max n chunk at {o}")
