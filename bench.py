@@ -313,8 +313,11 @@ def main() -> int:
                           "unpack_GBps_host_link": nb / unpack_s / 1e9,
                           "pack_ms": pack_s * 1e3, "unpack_ms": unpack_s * 1e3}
         result["ckpt"].update(async_pack_overlap(rcs, step, stream, w, m, v, buf, n))
-        result["ckpt"].update(file_write_rate(rcs, buf))
-        result["ckpt"].update(sharded_rate(rcs, w, m, v))
+        for leg in (lambda: file_write_rate(rcs, buf), lambda: sharded_rate(rcs, w, m, v)):
+            try:  # a full or read-only TMPDIR must not cost the step measurement
+                result["ckpt"].update(leg())
+            except (OSError, RuntimeError) as e:
+                result["ckpt"].setdefault("file_leg_errors", []).append(str(e))
         del buf
 
     if not args.no_cpu_baseline:
