@@ -457,3 +457,39 @@ def test_max_n_int32_limit_ragged_tail(dev):
         oracle.adamw_elems(ow, og, om, ov, float(s), float(bc1), float(bc2), float(decay), wl.lr)
         _check_state(w[o:o + chunk], m[o:o + chunk], v[o:o + chunk], ow, om, ov,
                      f"max n chunk at {o}")
+
+
+@pytest.mark.parametrize("case", ["clip_inf", "lr_zero", "wd_zero", "t_max", "zero_grad",
+                                  "inf_and_signed_zero_weights", "huge_grads", "tiny_lr"])
+def test_edge_scalars_and_values(dev, case):
+    n = 65_539
+    t, lr, wd, clip = 3, 3e-3, 0.01, 1.0
+    w = workloads.custom(400, n, 0.02, device=dev)
+    g = workloads.custom(401, n, 0.05, device=dev)
+    m = workloads.custom(402, n, 0.01, device=dev)
+    v = workloads.custom(403, n, 0.01, device=dev).square_()
+    if case == "clip_inf":
+        clip = float("inf")
+    elif case == "lr_zero":
+        lr = 0.0
+    elif case == "wd_zero":
+        wd = 0.0
+    elif case == "t_max":
+        t = 2**31 - 1  # bias corrections round to 1.0f
+    elif case == "zero_grad":
+        g.zero_()
+    elif case == "inf_and_signed_zero_weights":
+        w[:8] = torch.tensor([float("inf"), float("-inf"), 0.0, -0.0] * 2)
+    elif case == "huge_grads":
+        g.fill_(3e38)  # float32 squares overflow, the float64 sum does not
+    elif case == "tiny_lr":
+        lr = 1e-30
+    ow, og, om, ov = (_host(x).copy() for x in (w, g, m, v))
+    rcs.adamw_clip_step(w, g, m, v, t, lr, wd, clip)
+    gn = _gpu_norm()
+    rc, on = oracle.adamw_clip_step(ow, og, om, ov, t, lr, wd, clip)
+    assert rc == oracle.OK
+    assert gn == on == 0.0 if case == "zero_grad" else abs(gn - on) <= NORM_RTOL * on
+    _check_state(w, m, v, ow, om, ov, case)
+    if case == "lr_zero":
+        assert (_host(w) == _host(workloads.custom(400, n, 0.02, device=dev))).all()
