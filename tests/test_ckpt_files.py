@@ -28,7 +28,7 @@ def packed(step, n, seed=0):
     return torch.from_numpy(buf)
 
 
-def test_write_is_atomic_and_bytes_exact(tmp_path):
+def test_atomic_write_bytes_exact(tmp_path):
     buf = packed(80, 1001)
     path = rcs.ckpt_file_write(tmp_path, buf)
     assert os.path.basename(path) == "step_000080.bin"
