@@ -288,37 +288,84 @@ def signals_poll() -> int:
 class StepFileCheckpointer:
     """Step-file policy around a training loop: call after_step(t, w, m, v)
     after every completed update. It writes <dir>/step_NNNNNN.bin when t is a
-    multiple of `every`, when SIGUSR1 arrived (write and continue) or when
-    SIGTERM arrived (write, then after_step returns True: the caller exits),
-    keeps the newest `keep` files, and resume() loads the newest valid one."""
+    multiple of `every` (0 = never by cadence), when SIGUSR1 arrived (write and
+    continue) or when SIGTERM arrived (write, then after_step returns True:
+    the caller exits), keeps the newest `keep` files, and resume() loads the
+    newest valid one.
+
+    async_write=True takes the state with ckpt_pack_async (a device snapshot on
+    the training stream, drained on a copy stream) and writes the file from a
+    background thread, so training continues during both the host-link copy
+    and the disk write; the next save, a SIGTERM save and flush() wait for the
+    previous write first."""
 
     def __init__(self, directory, n: int, every: int = 100, keep: int = 3,
-                 install_signals: bool = True, stream=None):
+                 install_signals: bool = True, stream=None, async_write: bool = False):
+        import threading
+
         self.dir, self.n, self.every, self.keep = directory, int(n), int(every), int(keep)
         os.makedirs(directory, exist_ok=True)
         self.buf = torch.empty(ckpt_bytes(self.n), dtype=torch.uint8, pin_memory=True)
         self.stream = stream
         self.written: list[str] = []
+        self.async_write = bool(async_write)
+        self._thread: "threading.Thread | None" = None
+        self._error: BaseException | None = None
+        if self.async_write:
+            self.snapshot = torch.empty(ckpt_snapshot_bytes(self.n) // 4, dtype=torch.float32,
+                                        device="cuda")
+            self.copy_stream = torch.cuda.Stream()
         if install_signals:
             signals_install()
 
-    def save(self, t: int, w, m, v) -> str:
-        ckpt_pack(t, w, m, v, self.buf, stream=self.stream)
-        torch.cuda.synchronize()
+    def _finish(self) -> None:
         path = ckpt_file_write(self.dir, self.buf)
         self.written.append(path)
         ckpt_file_rotate(self.dir, self.keep)
-        return path
+
+    def _background(self) -> None:
+        try:
+            ckpt_pack_wait(self.snapshot)
+            self._finish()
+        except BaseException as e:  # surfaced by flush()
+            self._error = e
+
+    def flush(self) -> None:
+        """Waits for an asynchronous write in flight and re-raises its error."""
+        if self._thread is not None:
+            self._thread.join()
+            self._thread = None
+        if self._error is not None:
+            e, self._error = self._error, None
+            raise e
+
+    def save(self, t: int, w, m, v, wait: bool = False) -> None:
+        self.flush()
+        if not self.async_write:
+            ckpt_pack(t, w, m, v, self.buf, stream=self.stream)
+            torch.cuda.synchronize()
+            self._finish()
+            return
+        import threading
+
+        ckpt_pack_async(t, w, m, v, self.snapshot, self.buf, compute_stream=self.stream,
+                        copy_stream=self.copy_stream)
+        self._thread = threading.Thread(target=self._background, daemon=True)
+        self._thread.start()
+        if wait:
+            self.flush()
 
     def after_step(self, t: int, w, m, v) -> bool:
         sig = signals_poll()
+        exiting = bool(sig & SIG_WRITE_EXIT)
         if sig or (self.every > 0 and t % self.every == 0):
-            self.save(t, w, m, v)
-        return bool(sig & SIG_WRITE_EXIT)
+            self.save(t, w, m, v, wait=exiting)
+        return exiting
 
     def resume(self, w, m, v) -> int:
         """Loads the newest valid step file into w, m, v; returns its step
         (0 when there is none: a fresh run). Continue with t = step + 1."""
+        self.flush()
         found = ckpt_file_latest(self.dir)
         if found is None:
             return 0

@@ -1,6 +1,6 @@
 """Child process for the signal-driven resume test (not collected by pytest).
 
-usage: resume_child.py DIR WORKLOAD N TOTAL_STEPS USR1_AT TERM_AT
+usage: resume_child.py DIR WORKLOAD N TOTAL_STEPS USR1_AT TERM_AT [async]
 
 Resumes from the newest step file in DIR (or starts fresh), then runs updates
 until TOTAL_STEPS. It sends itself SIGUSR1 after update USR1_AT and SIGTERM
@@ -23,12 +23,13 @@ import workloads  # noqa: E402
 
 def main():
     d, name, n, total, usr1_at, term_at = sys.argv[1], sys.argv[2], *map(int, sys.argv[3:7])
+    async_write = len(sys.argv) > 7 and sys.argv[7] == "async"
     wl = workloads.WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.init_params(wl, device=dev, n=n)
     m, v = workloads.zeros_like_state(n, device=dev)
-    ck = rcs.StepFileCheckpointer(d, n, every=0, keep=3)
+    ck = rcs.StepFileCheckpointer(d, n, every=0, keep=3, async_write=async_write)
     start = ck.resume(w, m, v)
     print(f"child: resumed at step {start}", flush=True)
     g = torch.empty(n, device=dev)
@@ -42,7 +43,7 @@ def main():
         if ck.after_step(t, w, m, v):
             print(f"child: SIGTERM after step {t}, wrote {ck.written[-1]}", flush=True)
             return 0
-    ck.save(total, w, m, v)
+    ck.save(total, w, m, v, wait=True)
     print(f"child: finished {total}, wrote {ck.written[-1]}", flush=True)
     return 0
 

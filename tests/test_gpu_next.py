@@ -110,7 +110,8 @@ def _unpacked(buf, n):
             for j in range(3)]
 
 
-def test_signal_driven_step_files_resume_bit_identical(dev, tmp_path):
+@pytest.mark.parametrize("mode", ["sync", "async"])
+def test_signal_driven_step_files_resume_bit_identical(dev, tmp_path, mode):
     """A child trains, gets SIGUSR1 after step 30 (writes, continues) and
     SIGTERM after step 70 (writes, exits); a second child resumes from the
     newest file and finishes 100 steps. Its final state equals a straight run
@@ -119,13 +120,16 @@ def test_signal_driven_step_files_resume_bit_identical(dev, tmp_path):
     env = dict(os.environ)
     cmd = [sys.executable, "-u", os.path.join(HERE, "resume_child.py"), str(tmp_path), wl,
            str(n), str(total)]
-    r1 = subprocess.run(cmd + ["30", "70"], capture_output=True, text=True, timeout=240, env=env)
+    tail = [mode] if mode == "async" else []
+    r1 = subprocess.run(cmd + ["30", "70"] + tail, capture_output=True, text=True, timeout=240,
+                        env=env)
     print(r1.stdout, r1.stderr[-2000:])
     assert r1.returncode == 0
     assert "SIGTERM after step 70" in r1.stdout
     names = sorted(os.listdir(tmp_path))
     assert names == ["step_000030.bin", "step_000070.bin"], names
-    r2 = subprocess.run(cmd + ["0", "0"], capture_output=True, text=True, timeout=240, env=env)
+    r2 = subprocess.run(cmd + ["0", "0"] + tail, capture_output=True, text=True, timeout=240,
+                        env=env)
     print(r2.stdout, r2.stderr[-2000:])
     assert r2.returncode == 0 and "resumed at step 70" in r2.stdout
     final = open(tmp_path / "step_000100.bin", "rb").read()
