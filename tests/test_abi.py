@@ -136,3 +136,22 @@ def test_step_file_name():
     assert rcs.step_file_name(80) == "step_000080.bin"
     assert rcs.step_file_name(112700) == "step_112700.bin"
     assert rcs.step_file_name(1234567) == "step_1234567.bin"
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No CPU fallback: without librcs.so every entry point raises."""
+    monkeypatch.setattr(rcs, "LIB_PATH", "/nonexistent/librcs.so")
+    monkeypatch.setattr(rcs, "_lib", None)
+    with pytest.raises(ImportError):
+        rcs.lib()
+    with pytest.raises(ImportError):
+        rcs.ckpt_bytes(10)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
