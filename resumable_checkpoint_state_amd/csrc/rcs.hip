@@ -691,8 +691,7 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
         return RCS_EHIP;
     if (n % 4 == 0 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(snapshot)) {
         const int64_t total = 3 * (n >> 2);
-        int64_t blocks = (total + 255) / 256;
-        if (blocks > 65536) blocks = 65536;
+        const int64_t blocks = (total + 255) / 256;  // one vector per lane (at most 6.3M blocks)
         hipLaunchKernelGGL(ckpt_snapshot_vec, dim3((unsigned)blocks), dim3(256), 0, compute_stream,
                            reinterpret_cast<const f32x4 *>(w), reinterpret_cast<const f32x4 *>(m),
                            reinterpret_cast<const f32x4 *>(v), reinterpret_cast<f32x4 *>(snapshot),
