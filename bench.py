@@ -37,9 +37,17 @@ def _log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+HOST_SIDE_MARK = b"// ---------------------------------------------------------------- host side"
+
+
+def kernel_source_hash(text: bytes | None = None) -> str:
+    """sha256[:16] of the device part of rcs.hip (everything before its host
+    side: launch constants and kernels), so host-only edits keep the counters."""
+    if text is None:
+        with open(KERNEL_SRC, "rb") as f:
+            text = f.read()
+    cut = text.find(HOST_SIDE_MARK)
+    return hashlib.sha256(text if cut < 0 else text[:cut]).hexdigest()[:16]
 
 
 def measured_traffic():

@@ -419,7 +419,9 @@ int get_workspace(hipStream_t stream, Workspace **out) {
     return RCS_OK;
 }
 
-// The range [p, p + bytes) must lie inside one device allocation.
+// The range [p, p + bytes) must lie inside one device allocation. Memory the
+// runtime cannot report a range for (e.g. virtual-memory mappings) is accepted
+// when it is device or managed memory, without the length check.
 int check_device_range(const void *p, int64_t bytes) {
     if (p == nullptr) return RCS_EINVAL;
     hipDeviceptr_t base = nullptr;
@@ -687,7 +689,12 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
         ss = &e;
     }
     // the snapshot must not be overwritten while an earlier copy still reads it
-    if (ss->pending && hipStreamWaitEvent(compute_stream, ss->copied, 0) != hipSuccess)
+    bool pending = false;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        pending = ss->pending;
+    }
+    if (pending && hipStreamWaitEvent(compute_stream, ss->copied, 0) != hipSuccess)
         return RCS_EHIP;
     if (n % 4 == 0 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(snapshot)) {
         const int64_t total = 3 * (n >> 2);
@@ -713,6 +720,7 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
             hipSuccess ||
         hipEventRecord(ss->copied, copy_stream) != hipSuccess)
         return RCS_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
     ss->pending = true;
     return RCS_OK;
 }
@@ -756,21 +764,24 @@ int rcs_profile_enable(int on, int max_records, int every) {
 
 int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *steps) {
     if (!norm_ms_total || !update_ms_total || !steps) return RCS_EINVAL;
-    std::lock_guard<std::mutex> lk(g_mu);
+    std::vector<hipEvent_t> ev;
+    {  // copy the handles; wait on them without holding the library lock
+        std::lock_guard<std::mutex> lk(g_mu);
+        ev.assign(g_prof.ev.begin(), g_prof.ev.begin() + 3 * (size_t)g_prof.next);
+    }
     double a = 0.0, b = 0.0;
-    for (int i = 0; i < g_prof.next; ++i) {
-        hipEvent_t *e = &g_prof.ev[3 * i];
-        if (hipEventSynchronize(e[2]) != hipSuccess) return RCS_EHIP;
+    for (size_t i = 0; i + 2 < ev.size(); i += 3) {
+        if (hipEventSynchronize(ev[i + 2]) != hipSuccess) return RCS_EHIP;
         float x = 0.f, y = 0.f;
-        if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess ||
-            hipEventElapsedTime(&y, e[1], e[2]) != hipSuccess)
+        if (hipEventElapsedTime(&x, ev[i], ev[i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&y, ev[i + 1], ev[i + 2]) != hipSuccess)
             return RCS_EHIP;
         a += x;
         b += y;
     }
     *norm_ms_total = a;
     *update_ms_total = b;
-    *steps = g_prof.next;
+    *steps = (int64_t)(ev.size() / 3);
     return RCS_OK;
 }
 
