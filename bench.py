@@ -238,9 +238,9 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; the library records per-kernel HIP events on the
-    # stream the kernels run on, for one step in PROFILE_EVERY (their cost,
-    # about 12 us per recorded step, then adds ~1 us to the step average)
+    # timed region: K steps; on one step in PROFILE_EVERY the library has the
+    # kernel dispatches themselves stamp HIP events (start/end of the norm
+    # kernels and of the update kernel) on the stream they run on
     rcs.profile_enable(True, max(args.steps, 1), PROFILE_EVERY)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -216,10 +216,10 @@ int rcs_signals_install(void);
 int rcs_signals_poll(void);
 
 /*
- * Instrumentation: while enabled, adamw_clip_step records HIP events on its
- * stream around the norm kernels and around the update kernel, on one call in
- * `every` (the first call after enabling is recorded), up to max_records
- * recorded calls. rcs_profile_read synchronizes those events and returns the
+ * Instrumentation: while enabled, adamw_clip_step has its kernel dispatches
+ * stamp HIP events (start of grad_norm_partial, end of grad_norm_final, start
+ * and end of the update kernel) on one call in `every` (the first call after
+ * enabling is recorded), up to max_records recorded calls. rcs_profile_read synchronizes those events and returns the
  * summed milliseconds and the number of recorded calls. Enabling (or
  * disabling) discards earlier records. Events are created here, not in the
  * recorded calls.

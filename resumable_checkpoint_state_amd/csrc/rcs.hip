@@ -42,6 +42,7 @@
 // and without denormal flushing, so every float32 op is one IEEE
 // round-to-nearest-even operation, matching the sequence documented in rcs.h.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -410,7 +411,9 @@ struct Profile {
     int every = 1;       // record one step in `every`
     int64_t calls = 0;   // adamw_clip_step calls since enabling
     int next = 0;
-    std::vector<hipEvent_t> ev;  // 3 per recorded step
+    // 4 per recorded step: start of grad_norm_partial, end of grad_norm_final,
+    // start and end of the update kernel, stamped by the dispatches themselves
+    std::vector<hipEvent_t> ev;
 } g_prof;
 
 int get_workspace(hipStream_t stream, Workspace **out) {
@@ -483,30 +486,37 @@ int64_t norm_nt_limit4(int64_t n) {
     return n4 > tail4 ? n4 - tail4 : 0;
 }
 
+// ev (optional, profiling): ev[0] takes the partial kernel's start, ev[1] the
+// final kernel's end.
 int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *ws,
-                hipStream_t stream) {
+                hipStream_t stream, hipEvent_t *ev = nullptr) {
     const int nb = norm_blocks(n);
-    hipLaunchKernelGGL(grad_norm_partial, dim3(nb), dim3(kNormThreads), 0, stream, g, n,
-                       aligned16(g) ? 1 : 0, norm_nt_limit4(n), gscale, ws->partials);
-    hipLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream,
-                       (const double *)ws->partials, nb, clip, ws->scalars);
+    hipExtLaunchKernelGGL(grad_norm_partial, dim3(nb), dim3(kNormThreads), 0, stream,
+                          ev ? ev[0] : nullptr, nullptr, 0, g, n, aligned16(g) ? 1 : 0,
+                          norm_nt_limit4(n), gscale, ws->partials);
+    hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream, nullptr,
+                          ev ? ev[1] : nullptr, 0, (const double *)ws->partials, nb, clip,
+                          ws->scalars);
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
+// ev (optional, profiling): ev[0] and ev[1] take the update kernel's start and end.
 int launch_update(float *w, const float *g, float *m, float *v, int64_t n, const ClipScalars *sc,
-                  const StepScalars &h, hipStream_t stream) {
+                  const StepScalars &h, hipStream_t stream, hipEvent_t *ev = nullptr) {
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     if (aligned16(w) && aligned16(g) && aligned16(m) && aligned16(v)) {
         const int64_t n4 = n >> 2;
         int64_t blocks = (n4 + kUpdChunk - 1) / kUpdChunk;
         if (blocks < 1) blocks = 1;
-        hipLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream,
-                           reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
-                           reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n, sc, h);
+        hipExtLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
+                              stream, e0, e1, 0, reinterpret_cast<f32x4 *>(w),
+                              reinterpret_cast<const f32x4 *>(g), reinterpret_cast<f32x4 *>(m),
+                              reinterpret_cast<f32x4 *>(v), n, sc, h);
     } else {
         int64_t blocks = (n + kUpdThreads - 1) / kUpdThreads;
         if (blocks > 65536) blocks = 65536;
-        hipLaunchKernelGGL(adamw_update_scalar, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
-                           stream, w, g, m, v, n, sc, h);
+        hipExtLaunchKernelGGL(adamw_update_scalar, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
+                              stream, e0, e1, 0, w, g, m, v, n, sc, h);
     }
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
@@ -592,13 +602,10 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
     {
         std::lock_guard<std::mutex> lk(g_mu);
         if (g_prof.on && (g_prof.calls++ % g_prof.every) == 0 && g_prof.next < g_prof.max_records)
-            ev = &g_prof.ev[3 * g_prof.next++];
+            ev = &g_prof.ev[4 * g_prof.next++];
     }
-    if (ev) (void)hipEventRecord(ev[0], stream);
-    if ((rc = launch_norm(g, n, grad_scale, clip, ws, stream)) != RCS_OK) return rc;
-    if (ev) (void)hipEventRecord(ev[1], stream);
-    rc = launch_update(w, g, m, v, n, ws->scalars, h, stream);
-    if (ev) (void)hipEventRecord(ev[2], stream);
+    if ((rc = launch_norm(g, n, grad_scale, clip, ws, stream, ev)) != RCS_OK) return rc;
+    rc = launch_update(w, g, m, v, n, ws->scalars, h, stream, ev ? ev + 2 : nullptr);
     ws->has_norm = true;
     return rc;
 }
@@ -767,7 +774,7 @@ int rcs_profile_enable(int on, int max_records, int every) {
     if (!on) return RCS_OK;
     if (max_records < 1 || max_records > (1 << 20) || every < 1) return RCS_EINVAL;
     g_prof.every = every;
-    g_prof.ev.resize((size_t)3 * max_records);
+    g_prof.ev.resize((size_t)4 * max_records);
     for (auto &e : g_prof.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             (void)hipGetLastError();
@@ -784,21 +791,21 @@ int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *st
     std::vector<hipEvent_t> ev;
     {  // copy the handles; wait on them without holding the library lock
         std::lock_guard<std::mutex> lk(g_mu);
-        ev.assign(g_prof.ev.begin(), g_prof.ev.begin() + 3 * (size_t)g_prof.next);
+        ev.assign(g_prof.ev.begin(), g_prof.ev.begin() + 4 * (size_t)g_prof.next);
     }
     double a = 0.0, b = 0.0;
-    for (size_t i = 0; i + 2 < ev.size(); i += 3) {
-        if (hipEventSynchronize(ev[i + 2]) != hipSuccess) return RCS_EHIP;
+    for (size_t i = 0; i + 3 < ev.size(); i += 4) {
+        if (hipEventSynchronize(ev[i + 3]) != hipSuccess) return RCS_EHIP;
         float x = 0.f, y = 0.f;
         if (hipEventElapsedTime(&x, ev[i], ev[i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&y, ev[i + 1], ev[i + 2]) != hipSuccess)
+            hipEventElapsedTime(&y, ev[i + 2], ev[i + 3]) != hipSuccess)
             return RCS_EHIP;
         a += x;
         b += y;
     }
     *norm_ms_total = a;
     *update_ms_total = b;
-    *steps = (int64_t)(ev.size() / 3);
+    *steps = (int64_t)(ev.size() / 4);
     return RCS_OK;
 }
 
