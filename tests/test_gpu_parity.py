@@ -493,3 +493,31 @@ def test_edge_scalars_and_values(dev, case):
     _check_state(w, m, v, ow, om, ov, case)
     if case == "lr_zero":
         assert (_host(w) == _host(workloads.custom(400, n, 0.02, device=dev))).all()
+
+
+def test_two_streams_have_separate_workspaces(dev):
+    """Two parameter sets updated concurrently on two streams: each stream has
+    its own partials and clip scalars, so both match the oracle and each
+    stream's last_grad_norm is its own."""
+    n1, n2 = 1_000_003, 777_777
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    A = [workloads.custom(500 + k, n1, 0.02 if k == 0 else 0.0, device=dev) for k in range(3)]
+    B = [workloads.custom(510 + k, n2, 0.02 if k == 0 else 0.0, device=dev) for k in range(3)]
+    oA = [_host(x).copy() for x in A]
+    oB = [_host(x).copy() for x in B]
+    torch.cuda.synchronize()
+    for t in (1, 2, 3):
+        ga = workloads.custom(520 + t, n1, 0.05, device=dev)
+        gb = workloads.custom(530 + t, n2, 0.5, device=dev)
+        torch.cuda.synchronize()
+        rcs.adamw_clip_step(A[0], ga, A[1], A[2], t, 3e-3, 0.01, 1.0, stream=sa)
+        rcs.adamw_clip_step(B[0], gb, B[1], B[2], t, 1e-3, 0.1, 2.0, stream=sb)
+        na = rcs.last_grad_norm(stream=sa)
+        nb = rcs.last_grad_norm(stream=sb)
+        torch.cuda.synchronize()
+        _, ona = oracle.adamw_clip_step(oA[0], _host(ga), oA[1], oA[2], t, 3e-3, 0.01, 1.0)
+        _, onb = oracle.adamw_clip_step(oB[0], _host(gb), oB[1], oB[2], t, 1e-3, 0.1, 2.0)
+        assert abs(float(na.cpu()) - ona) <= NORM_RTOL * ona
+        assert abs(float(nb.cpu()) - onb) <= NORM_RTOL * onb
+    _check_state(*A, *oA, "stream A")
+    _check_state(*B, *oB, "stream B")
