@@ -48,3 +48,14 @@ def test_file_io_under_address_and_ub_sanitizers(tmp_path):
     d.mkdir()
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
     assert "ckpt_io driver ok" in _run([str(exe), str(d)], env=env)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_oracle_under_address_and_ub_sanitizers(tmp_path):
+    exe = tmp_path / "oracle_driver"
+    _run(["gcc", "-std=c11", "-g", "-O1", "-ffp-contract=off", "-fno-fast-math",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+          os.path.join(ROOT, "oracle", "oracle.c"), os.path.join(NATIVE, "oracle_driver.c"),
+          "-lm", "-o", str(exe)])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
+    assert "oracle driver ok" in _run([str(exe)], env=env)
