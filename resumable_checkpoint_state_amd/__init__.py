@@ -128,6 +128,9 @@ def _dev_f32(t: torch.Tensor, name: str, n: int | None = None) -> int:
         raise TypeError(f"{name} must be a contiguous float32 tensor")
     if n is not None and t.numel() != n:
         raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the library works on the current device "
+                         f"(cuda:{torch.cuda.current_device()}): use torch.cuda.device(...)")
     return t.data_ptr()
 
 
