@@ -195,9 +195,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the update path is per-GPU and this build "
-              "has no multi-GPU leg (see the sharding notes in DESIGN.md); run with --gpus 1",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the update path runs per GPU and no "
+              "multi-GPU leg (cross-GPU norm exchange, sharded state) is implemented; "
+              "run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
