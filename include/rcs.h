@@ -9,10 +9,12 @@
  * device. Results are valid once the stream reaches the enqueued work; the
  * caller must not touch the arrays or host buffers before then.
  *
- * The only memory the library owns is a per-(device, stream) workspace of
- * about 32 KiB (per-block float64 partial sums and the clip scalars). It is
- * allocated by rcs_init or on the first call that needs it, never inside a
- * later call, and lives until the process ends.
+ * The only device memory the library owns is a per-(device, stream)
+ * workspace of about 17 KiB (2048 per-block float64 partial sums and the clip
+ * scalars). It is allocated by rcs_init or on the first call that needs it,
+ * never inside a later call, and lives until the process ends. (The
+ * asynchronous pack also keeps two HIP events per snapshot buffer, and the
+ * instrumentation its events while enabled.)
  *
  * Every call validates its arguments on the host before enqueuing anything and
  * returns one of the status codes below; a negative return means nothing was
