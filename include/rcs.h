@@ -110,8 +110,20 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
 int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream);
 
 /*
- * Copies the pre-clip norm computed by the most recent adamw_clip_step or
- * grad_global_norm on this stream into norm_out (device or pinned host
+ * The global clip on its own, in place: the norm kernels as in
+ * adamw_clip_step, then the pages' third clip kernel (the grad_scale of the
+ * backprop lesson's pairing-rule table): g[i] = g[i] * s in float32 with
+ * s = (float)(clip/norm) if norm > clip, else 1. If the norm is not finite,
+ * g is left untouched. For callers that need the clipped gradient itself
+ * (adamw_clip_step never writes g). g: device float32[n]; clip > 0 (+inf
+ * never clips). 12 bytes of HBM traffic per element (norm read, scale read
+ * and write). The pre-clip norm is then available from last_grad_norm.
+ */
+int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream);
+
+/*
+ * Copies the pre-clip norm computed by the most recent adamw_clip_step,
+ * adamw_clip_step_accum, grad_clip_inplace or grad_global_norm on this stream into norm_out (device or pinned host
  * float64), in stream order. The resume lesson records this norm before the
  * clip to detect numerical faults. RCS_EINVAL if nothing ran on the stream.
  */

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_ckpt_header.restype = ctypes.c_int
         L.oracle_ckpt_unpack.argtypes = [u8p, i64, i64, ctypes.POINTER(i32), f32p, f32p, f32p]
         L.oracle_ckpt_unpack.restype = ctypes.c_int
+        L.oracle_clip_grads.argtypes = [f32p, i64, ctypes.c_float, f64p]
+        L.oracle_clip_grads.restype = ctypes.c_int
         L.oracle_scale_grads.argtypes = [f32p, i64, ctypes.c_float]
         L.oracle_scale_grads.restype = None
         L.oracle_subnormals_kept.argtypes = []
@@ -148,6 +150,13 @@ def adamw_clip_step(w, g, m, v, t: int, lr: float, wd: float, clip: float):
     norm = ctypes.c_double(0.0)
     rc = lib().oracle_adamw_clip_step(_f32(w, True), _f32(g), _f32(m, True), _f32(v, True), n,
                                       t, lr, wd, clip, ctypes.byref(norm))
+    return rc, norm.value
+
+
+def clip_grads(g: np.ndarray, clip: float):
+    """In place global clip; returns (status, pre-clip norm)."""
+    norm = ctypes.c_double(0.0)
+    rc = lib().oracle_clip_grads(_f32(g, True), g.size, clip, ctypes.byref(norm))
     return rc, norm.value
 
 

@@ -84,7 +84,13 @@ void oracle_sumsq_accum(double state[2], const float *g, int64_t n) {
     state[1] = comp;
 }
 
-double oracle_sumsq_finish(const double state[2]) { return state[0] + state[1]; }
+/* A non-finite running sum (an infinite or NaN square) is returned as is: the
+ * compensation term is then meaningless (inf - inf), and the plain definition
+ * of the norm of a vector holding +-inf is +inf, of one holding NaN, NaN. */
+double oracle_sumsq_finish(const double state[2]) {
+    if (!isfinite(state[0])) return state[0];
+    return state[0] + state[1];
+}
 
 double oracle_grad_norm(const float *g, int64_t n) {
     double st[2] = {0.0, 0.0};
@@ -136,6 +142,17 @@ void oracle_adamw_elems(float *w, const float *g, float *m, float *v, int64_t n,
  * multiply) before the optimizer step. */
 void oracle_scale_grads(float *g, int64_t n, float scale) {
     for (int64_t i = 0; i < n; ++i) g[i] = g[i] * scale;
+}
+
+/* The global clip alone, in place (R1-R3): g[i] = g[i] * s, skipped when the
+ * norm is not finite. Returns ORACLE_OK or ORACLE_SKIPPED. */
+int oracle_clip_grads(float *g, int64_t n, float clip, double *norm_out) {
+    double norm = oracle_grad_norm(g, n);
+    if (norm_out) *norm_out = norm;
+    if (!isfinite(norm)) return ORACLE_SKIPPED;
+    float s = oracle_clip_scale(norm, clip);
+    for (int64_t i = 0; i < n; ++i) g[i] = g[i] * s;
+    return ORACLE_OK;
 }
 
 /* One full update: norm, clip factor, scalars, elementwise step.

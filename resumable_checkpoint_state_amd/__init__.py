@@ -19,7 +19,7 @@ from ._build import LIB as LIB_PATH
 from ._build import build
 
 __all__ = [
-    "RcsError", "adamw_clip_step", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
+    "RcsError", "adamw_clip_step", "adamw_clip_step_accum", "grad_clip_inplace", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
     "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read", "fp32_div_sqrt_probe",
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
 ]
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.rcs_fp32_div_sqrt_probe.restype = ctypes.c_int
     L.adamw_clip_step_accum.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, f32, vp]
     L.adamw_clip_step_accum.restype = ctypes.c_int
+    L.grad_clip_inplace.argtypes = [f32p, i64, f32, vp]
+    L.grad_clip_inplace.restype = ctypes.c_int
     L.ckpt_snapshot_bytes.argtypes = [i64]
     L.ckpt_snapshot_bytes.restype = i64
     L.ckpt_pack_async.argtypes = [i32, i64, f32p, f32p, f32p, f32p, i64, vp, i64, vp, vp]
@@ -158,6 +160,12 @@ def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: fl
     _check(lib().adamw_clip_step_accum(*args, n, int(t), float(lr), float(wd), float(clip),
                                        float(grad_scale), _stream(stream)),
            "adamw_clip_step_accum")
+
+
+def grad_clip_inplace(g, clip: float, stream=None) -> None:
+    """g *= clip/||g|| in place when ||g|| > clip (the global clip on its own)."""
+    _check(lib().grad_clip_inplace(_dev_f32(g, "g"), g.numel(), float(clip), _stream(stream)),
+           "grad_clip_inplace")
 
 
 def _norm_out(out):

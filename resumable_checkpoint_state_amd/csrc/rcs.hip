@@ -356,6 +356,32 @@ __global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restri
     }
 }
 
+// The pages' third clip kernel on its own, for callers that need the clipped
+// gradient itself: g *= s in place (skipped when the norm is not finite).
+// Same float32 product as the update's g * s.
+__global__ __launch_bounds__(256) void grad_scale_vec(f32x4 *__restrict__ g, int64_t n4,
+                                                      const ClipScalars *__restrict__ sc) {
+    if (!sc->apply) return;
+    const float s = sc->scale;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) {
+        f32x4 x = __builtin_nontemporal_load(g + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = x[k] * s;
+        __builtin_nontemporal_store(x, g + i);
+    }
+}
+
+__global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, int64_t begin,
+                                                         int64_t n,
+                                                         const ClipScalars *__restrict__ sc) {
+    if (!sc->apply) return;
+    const float s = sc->scale;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = begin + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+        g[i] = g[i] * s;
+}
+
 // a4 (asynchronous form): copy w, m, v into one device snapshot laid out like
 // the step file's payload [w | m | v], so that the training stream can keep
 // updating w, m, v while the snapshot drains to the host on a copy stream.
@@ -622,6 +648,33 @@ int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t st
         hipSuccess)
         return RCS_EHIP;
     return RCS_OK;
+}
+
+int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream) {
+    if (!valid_n(n)) return RCS_EINVAL;
+    if (std::isnan(clip) || !(clip > 0.0f)) return RCS_EINVAL;
+    int rc;
+    if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
+    Workspace *ws = nullptr;
+    if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
+    if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
+    ws->has_norm = true;
+    int64_t done = 0;
+    if (aligned16(g)) {
+        const int64_t n4 = n >> 2;
+        if (n4 > 0)
+            hipLaunchKernelGGL(grad_scale_vec, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                               stream, reinterpret_cast<f32x4 *>(g), n4,
+                               (const ClipScalars *)ws->scalars);
+        done = n4 << 2;
+    }
+    if (done < n) {
+        int64_t blocks = (n - done + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(grad_scale_scalar, dim3((unsigned)blocks), dim3(256), 0, stream, g,
+                           done, n, (const ClipScalars *)ws->scalars);
+    }
+    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
 int last_grad_norm(hipStream_t stream, double *norm_out) {

@@ -521,3 +521,26 @@ def test_two_streams_have_separate_workspaces(dev):
         assert abs(float(nb.cpu()) - onb) <= NORM_RTOL * onb
     _check_state(*A, *oA, "stream A")
     _check_state(*B, *oB, "stream B")
+
+
+@pytest.mark.parametrize("n,offset,sigma", [(1, 0, 5.0), (7, 0, 5.0), (262_147, 0, 0.01),
+                                            (1_000_003, 0, 1.0), (100_001, 1, 1.0),
+                                            (12_800_000, 0, 1e-4)])
+def test_grad_clip_inplace_parity(dev, n, offset, sigma):
+    base = workloads.custom(600, n + offset, sigma, device=dev)
+    g = base[offset:]
+    og = _host(g).copy()
+    rcs.grad_clip_inplace(g, 1.0)
+    gn = _gpu_norm()
+    rc, on = oracle.clip_grads(og, 1.0)
+    assert rc == oracle.OK and abs(gn - on) <= NORM_RTOL * on
+    assert max_ulp(_host(g), og) <= ULP_TOL
+
+
+def test_grad_clip_inplace_nonfinite_untouched(dev):
+    g = workloads.custom(601, 10_000, 1.0, device=dev)
+    g[5] = float("nan")
+    before = _host(g).copy()
+    rcs.grad_clip_inplace(g, 1.0)
+    assert not np.isfinite(_gpu_norm())
+    assert (bits(_host(g)) == bits(before)).all()

@@ -178,6 +178,7 @@ def test_norm_nonfinite_skips_update():
         w0, m0, v0 = w.copy(), m.copy(), v.copy()
         rc, norm = oracle.adamw_clip_step(w, g, m, v, 5, 1e-3, 0.01, 1.0)
         assert rc == oracle.SKIPPED and not math.isfinite(norm)
+        assert (norm == math.inf) if not np.isnan(bad) else math.isnan(norm)
         assert (f32bits(w) == f32bits(w0)).all() and (f32bits(m) == f32bits(m0)).all()
         assert (f32bits(v) == f32bits(v0)).all()
     # huge finite values overflow the float32 square but not the float64 sum
@@ -440,3 +441,37 @@ def test_scale_grads_averages_accumulated_microbatches():
     oracle.adamw_clip_step_accum(w1, (g + g).astype(np.float32), m1, v1, 1, 3e-3, 0.01, 1.0, 0.5)
     oracle.adamw_clip_step(w2, g, m2, v2, 1, 3e-3, 0.01, 1.0)
     assert (f32bits(w1) == f32bits(w2)).all() and (f32bits(m1) == f32bits(m2)).all()
+
+
+# ---------------------------------------------------------------- the clip on its own
+
+def test_clip_grads_matches_torch_and_the_update_path():
+    rng = np.random.default_rng(41)
+    for sigma, clip in [(0.01, 1.0), (1.0, 1.0), (3.0, 0.25), (1e-4, 1.0)]:
+        g = (rng.standard_normal(30_000) * sigma).astype(np.float32)
+        g0 = g.copy()
+        rc, norm = oracle.clip_grads(g, clip)
+        assert rc == oracle.OK
+        # PyTorch's clip in float64 (its factor has +1e-6 in the denominator)
+        p = torch.nn.Parameter(torch.zeros(g.size, dtype=torch.float64))
+        p.grad = torch.from_numpy(g0.astype(np.float64))
+        total = float(torch.nn.utils.clip_grad_norm_([p], max_norm=clip))
+        assert norm == pytest.approx(total, rel=1e-13)
+        assert np.allclose(g, p.grad.numpy(), rtol=2e-6 + 2e-6 / norm, atol=0)
+        if norm <= clip:
+            assert (f32bits(g) == f32bits(g0)).all()
+        else:
+            assert np.sqrt(np.sum(g.astype(np.float64) ** 2)) <= clip * (1 + 8 * 2.0 ** -24)
+        # the update applies the same clipped gradient: at t = 1 with m = 0, m = 0.1f * g'
+        w, m, v = np.zeros_like(g0), np.zeros_like(g0), np.zeros_like(g0)
+        oracle.adamw_clip_step(w, g0, m, v, 1, 1e-3, 0.0, clip)
+        assert (f32bits(m) == f32bits(np.float32(0.1) * g)).all()
+
+
+def test_clip_grads_nonfinite_leaves_gradient():
+    g = np.ones(100, np.float32)
+    g[7] = np.inf
+    g0 = g.copy()
+    rc, norm = oracle.clip_grads(g, 1.0)
+    assert rc == oracle.SKIPPED and norm == np.inf
+    assert (f32bits(g) == f32bits(g0)).all()
