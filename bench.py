@@ -299,6 +299,16 @@ def main() -> int:
                      "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
     }
 
+    # the clip on its own (norm kernels + in-place scale), 12 B/param
+    reps = 10
+    ev0.record(stream)
+    for _ in range(reps):
+        rcs.grad_clip_inplace(grads[0], wl.clip, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    clip_s = ev0.elapsed_time(ev1) / reps / 1e3
+    result["grad_clip_inplace"] = {"us": clip_s * 1e6, "GBps_12B_per_param": 12 * n / clip_s / 1e9}
+
     if not args.no_ckpt:
         nb = rcs.ckpt_bytes(n)
         buf = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
