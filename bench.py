@@ -75,16 +75,31 @@ def cpu_baseline(wl, budget_s: float):
     w = workloads.init_params(wl).numpy()
     m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
     g = workloads.grads(wl, 1).numpy()
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.adamw_clip_step(w, g, m, v, steps + 1, wl.lr, wl.wd, wl.clip)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 100:
-            break
+    cpu_model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    allowed = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {allowed[-1]})  # one core for the single-threaded oracle
+    try:
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.adamw_clip_step(w, g, m, v, steps + 1, wl.lr, wl.wd, wl.clip)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or steps >= 100:
+                break
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     return {"value": n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full {wl.name} steps (n={n:,}) on one host thread, "
-                      f"{el:.1f} s"}
+            "sample": f"{steps} full {wl.name} steps (n={n:,}) on one host thread pinned to "
+                      f"core {allowed[-1]}, {el:.1f} s",
+            "host_cpu": cpu_model, "host_cores_available": len(allowed),
+            "GBps_32B_per_param": 32 * n * steps / el / 1e9}
 
 
 def async_pack_overlap(rcs, step, stream, w, m, v, buf, n, k=60):
@@ -267,6 +282,18 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_step_noev = ev0.elapsed_time(ev1) / args.steps
 
+    # a third pass with an event between consecutive steps: per-step spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for k in range(args.steps):
+        step()
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(args.steps))
+    step_median_us = per_step[len(per_step) // 2]
+    step_p90_us = per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)]
+
     upd_s = upd_ms / rec / 1e3
     norm_s = norm_ms / rec / 1e3
     achieved = UPDATE_BYTES_PER_PARAM * n / upd_s / 1e9
@@ -293,6 +320,8 @@ def main() -> int:
         "model_frac_of_hbm_peak": model_gbps / HBM_PEAK_GBPS,
         "kernels_us": {"norm_partial_plus_final": norm_s * 1e6, "adamw_update": upd_s * 1e6},
         "ms_per_step_without_kernel_events": ms_step_noev,
+        "step_us_median": step_median_us,
+        "step_us_p90": step_p90_us,
         "roofline": {"bound": "hbm", "kernel": "adamw_update_vec", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(),
