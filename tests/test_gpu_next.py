@@ -145,3 +145,27 @@ def test_signal_driven_step_files_resume_bit_identical(dev, tmp_path, mode):
     rcs.ckpt_pack(total, w, m, v, buf)
     torch.cuda.synchronize()
     assert buf.numpy().tobytes() == final
+
+
+def test_weights_only_resume_diverges(dev):
+    """Why m and v are in the file: resuming from the weights alone (m = v = 0,
+    t restarted at 1) takes a different trajectory from the full resume,
+    which is byte-identical to the straight run."""
+    wl = workloads.WORKLOADS["flat262k"]
+    n, k, total = wl.n, 40, 50
+    w = workloads.init_params(wl, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    g = torch.empty(n, device=dev)
+    for t in range(1, k + 1):
+        workloads.grads(wl, t, device=dev, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+    full = [w.clone(), m.clone(), v.clone()]
+    weights_only = [w.clone(), torch.zeros_like(m), torch.zeros_like(v)]
+    for t in range(k + 1, total + 1):
+        workloads.grads(wl, t, device=dev, out=g)
+        rcs.adamw_clip_step(full[0], g, full[1], full[2], t, wl.lr, wl.wd, wl.clip)
+        rcs.adamw_clip_step(weights_only[0], g, weights_only[1], weights_only[2], t - k,
+                            wl.lr, wl.wd, wl.clip)
+    torch.cuda.synchronize()
+    diff = (full[0] - weights_only[0]).abs().max().item()
+    assert diff > 10 * wl.lr, diff  # the first restarted step alone moves w by about lr
