@@ -544,3 +544,28 @@ def test_grad_clip_inplace_nonfinite_untouched(dev):
     rcs.grad_clip_inplace(g, 1.0)
     assert not np.isfinite(_gpu_norm())
     assert (bits(_host(g)) == bits(before)).all()
+
+
+def test_gpu_path_is_deterministic(dev):
+    """The reduction order depends only on n: two runs from the same state
+    give the same bytes, and the same norm bit for bit, every time."""
+    wl = workloads.WORKLOADS["andrea12m"]
+    n = wl.n
+    outs, norms = [], []
+    for _ in range(2):
+        w = workloads.init_params(wl, device=dev)
+        m, v = workloads.zeros_like_state(n, device=dev)
+        g = torch.empty(n, device=dev)
+        run_norms = []
+        for t in range(1, 6):
+            workloads.grads(wl, t, device=dev, out=g)
+            rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+            run_norms.append(_gpu_norm())
+        outs.append([_host(x).copy() for x in (w, m, v)])
+        norms.append(run_norms)
+    assert norms[0] == norms[1]
+    for a, b in zip(*outs):
+        assert (bits(a) == bits(b)).all()
+    g = workloads.custom(700, n, 1.0, device=dev)
+    vals = {float(rcs.grad_global_norm(g).cpu()) for _ in range(5)}
+    assert len(vals) == 1
