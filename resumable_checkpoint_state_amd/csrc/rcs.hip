@@ -465,11 +465,20 @@ int get_workspace(hipStream_t stream, Workspace **out) {
     return RCS_OK;
 }
 
-// The range [p, p + bytes) must lie inside one device allocation. Memory the
-// runtime cannot report a range for (e.g. virtual-memory mappings) is accepted
-// when it is device or managed memory, without the length check.
+// p must be device (or managed) memory of the current device and the range
+// [p, p + bytes) must lie inside one allocation. Memory the runtime cannot
+// report a range for (e.g. virtual-memory mappings) is accepted without the
+// length check.
 int check_device_range(const void *p, int64_t bytes) {
     if (p == nullptr) return RCS_EINVAL;
+    int dev = -1;
+    hipPointerAttribute_t pa;
+    if (hipGetDevice(&dev) != hipSuccess || hipPointerGetAttributes(&pa, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return RCS_EINVAL;
+    }
+    if (pa.type != hipMemoryTypeDevice && pa.type != hipMemoryTypeManaged) return RCS_EINVAL;
+    if (pa.type == hipMemoryTypeDevice && pa.device != dev) return RCS_EINVAL;  // another GPU's
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
     if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) == hipSuccess && base) {
@@ -479,13 +488,7 @@ int check_device_range(const void *p, int64_t bytes) {
         return RCS_OK;
     }
     (void)hipGetLastError();
-    hipPointerAttribute_t attr;
-    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
-        (void)hipGetLastError();
-        return RCS_EINVAL;
-    }
-    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return RCS_EINVAL;
-    return RCS_OK;
+    return RCS_OK;  // device memory without a reportable range: accepted, length unchecked
 }
 
 bool overlaps(const void *a, const void *b, int64_t bytes) {

@@ -569,3 +569,21 @@ def test_gpu_path_is_deterministic(dev):
     g = workloads.custom(700, n, 1.0, device=dev)
     vals = {float(rcs.grad_global_norm(g).cpu()) for _ in range(5)}
     assert len(vals) == 1
+
+
+def test_abi_rejects_host_and_short_device_buffers(dev):
+    """Host-side checks at the C boundary: pinned host memory is not device
+    memory, and a device array shorter than n is refused before any launch."""
+    L = rcs.lib()
+    n = 4096
+    host = torch.zeros(n, dtype=torch.float32, pin_memory=True)
+    d = [torch.zeros(n, device=dev) for _ in range(4)]
+    p = [x.data_ptr() for x in d]
+    stream = torch.cuda.current_stream().cuda_stream
+    assert L.adamw_clip_step(host.data_ptr(), p[1], p[2], p[3], n, 1, 1e-3, 0.0, 1.0,
+                             stream) == rcs.EINVAL
+    short = torch.zeros(n // 2, device=dev)
+    rc = L.adamw_clip_step(p[0], short.data_ptr(), p[2], p[3], n, 1, 1e-3, 0.0, 1.0, stream)
+    assert rc in (rcs.ESIZE, rcs.OK)  # ESIZE unless the allocator packed it inside a larger block
+    assert L.adamw_clip_step(p[0], p[0], p[2], p[3], n, 1, 1e-3, 0.0, 1.0, stream) == rcs.EINVAL
+    torch.cuda.synchronize()
