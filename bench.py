@@ -42,12 +42,17 @@ HOST_SIDE_MARK = b"// ----------------------------------------------------------
 
 def kernel_source_hash(text: bytes | None = None) -> str:
     """sha256[:16] of the device part of rcs.hip (everything before its host
-    side: launch constants and kernels), so host-only edits keep the counters."""
+    side: launch constants and kernels) with comments and whitespace runs
+    removed, so host-only and comment-only edits keep the counters."""
     if text is None:
         with open(KERNEL_SRC, "rb") as f:
             text = f.read()
     cut = text.find(HOST_SIDE_MARK)
-    return hashlib.sha256(text if cut < 0 else text[:cut]).hexdigest()[:16]
+    code = text if cut < 0 else text[:cut]
+    code = re.sub(rb"/\*.*?\*/", b" ", code, flags=re.S)  # the device part has no string literals
+    code = re.sub(rb"//[^\n]*", b" ", code)
+    code = re.sub(rb"\s+", b" ", code).strip()
+    return hashlib.sha256(code).hexdigest()[:16]
 
 
 def measured_traffic():

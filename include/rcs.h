@@ -84,7 +84,9 @@ int rcs_init(int device, hipStream_t stream);
  * left untouched); read the norm with last_grad_norm.
  * The reduction order depends only on n, so results are deterministic.
  * 16-byte aligned arrays take the vector path; others a scalar path with the
- * same arithmetic.
+ * same arithmetic. With aligned arrays and 4 <= n <= 4,194,304 the final
+ * reduction runs inside the update kernel (two launches instead of three;
+ * same reduction order, so the same norm bits as grad_global_norm).
  */
 int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                     float lr, float wd, float clip, hipStream_t stream);
@@ -231,8 +233,9 @@ int rcs_signals_poll(void);
 
 /*
  * Instrumentation: while enabled, adamw_clip_step has its kernel dispatches
- * stamp HIP events (start of grad_norm_partial, end of grad_norm_final, start
- * and end of the update kernel) on one call in `every` (the first call after
+ * stamp HIP events (start of grad_norm_partial, end of grad_norm_final -- or
+ * of grad_norm_partial when the update kernel does the final reduction --,
+ * start and end of the update kernel) on one call in `every` (the first call after
  * enabling is recorded), up to max_records recorded calls. rcs_profile_read synchronizes those events and returns the
  * summed milliseconds and the number of recorded calls. Enabling (or
  * disabling) discards earlier records. Events are created here, not in the

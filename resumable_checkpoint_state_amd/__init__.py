@@ -115,24 +115,35 @@ def _check(rc: int, where: str) -> int:
     return rc
 
 
-def _stream(stream) -> int:
+# The current stream's raw handle without building a torch.cuda.Stream object
+# (a few microseconds per call, which matters for small updates).
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device: int | None = None) -> int:
     if stream is None:
+        if _raw_current_stream is not None:
+            return _raw_current_stream(torch.cuda.current_device() if device is None else device)
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
 
 
-def _dev_f32(t: torch.Tensor, name: str, n: int | None = None) -> int:
+def _dev_f32(t: torch.Tensor, name: str, n: int | None = None, cur: int | None = None) -> int:
+    """Device pointer of a contiguous float32 tensor on the current device
+    (cur: the current device index, when the caller already has it)."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
     if t.dtype != torch.float32 or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous float32 tensor")
     if n is not None and t.numel() != n:
         raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
-    if t.device.index != torch.cuda.current_device():
+    if cur is None:
+        cur = torch.cuda.current_device()
+    if t.get_device() != cur:
         raise ValueError(f"{name} is on {t.device}; the library works on the current device "
-                         f"(cuda:{torch.cuda.current_device()}): use torch.cuda.device(...)")
+                         f"(cuda:{cur}): use torch.cuda.device(...)")
     return t.data_ptr()
 
 
@@ -144,10 +155,11 @@ def init(device: int | None = None, stream=None) -> None:
 
 def adamw_clip_step(w, g, m, v, t: int, lr: float, wd: float, clip: float, stream=None) -> None:
     """One clipped AdamW update of w, m, v in place (asynchronous on stream)."""
-    n = w.numel()
-    args = (_dev_f32(w, "w"), _dev_f32(g, "g", n), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    n, wp = w.numel(), _dev_f32(w, "w")
+    cur = w.get_device()  # the current device, checked just above
+    args = (wp, _dev_f32(g, "g", n, cur), _dev_f32(m, "m", n, cur), _dev_f32(v, "v", n, cur))
     _check(lib().adamw_clip_step(*args, n, int(t), float(lr), float(wd), float(clip),
-                                 _stream(stream)), "adamw_clip_step")
+                                 _stream(stream, cur)), "adamw_clip_step")
 
 
 def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: float,
@@ -155,10 +167,11 @@ def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: fl
     """The update for a gradient summed over micro-batches: each element of
     g_sum is multiplied by the float32 grad_scale (1/n_micro) inside the
     kernels before norm, clip and update; g_sum is not written."""
-    n = w.numel()
-    args = (_dev_f32(w, "w"), _dev_f32(g_sum, "g", n), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+    n, wp = w.numel(), _dev_f32(w, "w")
+    cur = w.get_device()
+    args = (wp, _dev_f32(g_sum, "g", n, cur), _dev_f32(m, "m", n, cur), _dev_f32(v, "v", n, cur))
     _check(lib().adamw_clip_step_accum(*args, n, int(t), float(lr), float(wd), float(clip),
-                                       float(grad_scale), _stream(stream)),
+                                       float(grad_scale), _stream(stream, cur)),
            "adamw_clip_step_accum")
 
 

@@ -35,6 +35,10 @@
 //     XCDs), which evens out DRAM contention between the seven streams. The
 //     clip factor is read from device memory, so the host never waits between
 //     kernels.
+//   * adamw_update_vec_fold: for small n (at most 256 partials) the update
+//     kernel does grad_norm_final's reduction at its head, so the step costs
+//     two launches, not three; below a few million elements the step is bound
+//     by the runtime's per-launch host cost, not by HBM.
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -45,6 +49,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -74,6 +79,12 @@
 #endif
 #ifndef RCS_UPD_NT
 #define RCS_UPD_NT 1
+#endif
+// Steps whose norm pass has at most 256 partials (n <= 4,194,304) and whose
+// arrays are 16-byte aligned fold the final reduction into the update kernel:
+// two launches instead of three. 0 keeps three launches at every size.
+#ifndef RCS_FOLD_FINAL
+#define RCS_FOLD_FINAL 1
 #endif
 // Bytes at the end of g that the norm pass reads with ordinary (cache-
 // allocating) loads so that the update, which reads g again right after,
@@ -329,6 +340,69 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
     }
 }
 
+// a2 + a3 for small n (at most kFoldMaxParts partials): every block reduces the
+// partials itself, so the step is two launches instead of three. Lane i takes
+// partial i (0 beyond nparts) and the block sums in the same wave/LDS order as
+// grad_norm_final, whose extra lanes and waves only add +0.0 to a
+// non-negative sum: norm, clip factor and flag are the same bits. Block 0
+// also stores the record for last_grad_norm. The element loads are in flight
+// while the block reduces.
+constexpr int kFoldMaxParts = kUpdThreads;
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
+    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ v, int64_t n, const double *__restrict__ partials, int nparts, float clip,
+    ClipScalars *__restrict__ sc_out, StepScalars h) {
+    __shared__ double lds[kUpdThreads / kWave];
+    __shared__ float s_scale;
+    __shared__ int s_apply;
+    const int64_t n4 = n >> 2;
+    const int64_t i = (int64_t)blockIdx.x * kUpdThreads + threadIdx.x;
+    // Unconditional loads, the partial first, so that waiting for it leaves
+    // the four element loads in flight (lanes past the end re-read the last
+    // partial / vector and discard it; the host guarantees n >= 4).
+    const int tp = (int)threadIdx.x < nparts ? (int)threadIdx.x : nparts - 1;
+    const double xp = partials[tp];
+    const int64_t ic = i < n4 ? i : n4 - 1;
+    f32x4 gr = ld_stream(g + ic);
+    f32x4 wr = ld_stream(w + ic);
+    f32x4 mr = ld_stream(m + ic);
+    f32x4 vr = ld_stream(v + ic);
+    const double x = ((int)threadIdx.x < nparts) ? xp : 0.0;
+    const double S = block_sum<kUpdThreads>(x, lds);
+    if (threadIdx.x == 0) {
+        const double norm = sqrt(S);
+        ClipScalars r;
+        r.norm = norm;
+        r.apply = isfinite(norm) ? 1 : 0;
+        r.scale = (norm > (double)clip) ? (float)((double)clip / norm) : 1.0f;
+        s_scale = r.scale;
+        s_apply = r.apply;
+        if (blockIdx.x == 0) *sc_out = r;
+    }
+    __syncthreads();
+    if (!s_apply) return;
+    const float s = s_scale;
+    if (i < n4) {
+        adamw_vec4(wr, gr, mr, vr, s, h);
+        st_stream(w + i, wr);
+        st_stream(m + i, mr);
+        st_stream(v + i, vr);
+    }
+    const int rem = (int)(n & 3);
+    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
+        const int64_t k = (n4 << 2) + threadIdx.x;
+        float *wf = reinterpret_cast<float *>(w);
+        float *mf = reinterpret_cast<float *>(m);
+        float *vf = reinterpret_cast<float *>(v);
+        const float *gf = reinterpret_cast<const float *>(g);
+        float ww = wf[k], mm = mf[k], vv = vf[k];
+        adamw_elem(ww, gf[k], mm, vv, s, h);
+        wf[k] = ww;
+        mf[k] = mm;
+        vf[k] = vv;
+    }
+}
+
 // a3 for arrays that are not all 16-byte aligned: same arithmetic per element.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_scalar(
     float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
@@ -416,7 +490,7 @@ __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restr
 struct Workspace {
     double *partials = nullptr;      // kNormMaxBlocks float64
     ClipScalars *scalars = nullptr;  // one record
-    bool has_norm = false;
+    std::atomic<bool> has_norm{false};
 };
 
 std::mutex g_mu;
@@ -456,10 +530,10 @@ int get_workspace(hipStream_t stream, Workspace **out) {
             return RCS_ENOMEM;
         }
         char *base = static_cast<char *>(p);
-        Workspace ws;
-        ws.partials = reinterpret_cast<double *>(base);
-        ws.scalars = reinterpret_cast<ClipScalars *>(base + (size_t)kNormMaxBlocks * sizeof(double));
-        it = g_ws.emplace(key, ws).first;
+        it = g_ws.try_emplace(key).first;
+        it->second.partials = reinterpret_cast<double *>(base);
+        it->second.scalars =
+            reinterpret_cast<ClipScalars *>(base + (size_t)kNormMaxBlocks * sizeof(double));
     }
     *out = &it->second;
     return RCS_OK;
@@ -515,17 +589,49 @@ int64_t norm_nt_limit4(int64_t n) {
     return n4 > tail4 ? n4 - tail4 : 0;
 }
 
-// ev (optional, profiling): ev[0] takes the partial kernel's start, ev[1] the
-// final kernel's end.
+// a1 alone. ev0 / ev1 (optional, profiling) take the kernel's start / end.
+void launch_partial(const float *g, int64_t n, float gscale, Workspace *ws, hipStream_t stream,
+                    hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+    hipExtLaunchKernelGGL(grad_norm_partial, dim3(norm_blocks(n)), dim3(kNormThreads), 0, stream,
+                          ev0, ev1, 0, g, n, aligned16(g) ? 1 : 0, norm_nt_limit4(n), gscale,
+                          ws->partials);
+}
+
+// a1 + a2. ev (optional, profiling): ev[0] takes the partial kernel's start,
+// ev[1] the final kernel's end.
 int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *ws,
                 hipStream_t stream, hipEvent_t *ev = nullptr) {
-    const int nb = norm_blocks(n);
-    hipExtLaunchKernelGGL(grad_norm_partial, dim3(nb), dim3(kNormThreads), 0, stream,
-                          ev ? ev[0] : nullptr, nullptr, 0, g, n, aligned16(g) ? 1 : 0,
-                          norm_nt_limit4(n), gscale, ws->partials);
+    launch_partial(g, n, gscale, ws, stream, ev ? ev[0] : nullptr);
     hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream, nullptr,
-                          ev ? ev[1] : nullptr, 0, (const double *)ws->partials, nb, clip,
-                          ws->scalars);
+                          ev ? ev[1] : nullptr, 0, (const double *)ws->partials, norm_blocks(n),
+                          clip, ws->scalars);
+    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
+}
+
+bool all_aligned16(const void *a, const void *b, const void *c, const void *d) {
+    return aligned16(a) && aligned16(b) && aligned16(c) && aligned16(d);
+}
+
+// Whether the step takes the two-launch form (a2 folded into the update).
+bool fold_final(const float *w, const float *g, const float *m, const float *v, int64_t n) {
+    return RCS_FOLD_FINAL && n >= 4 && norm_blocks(n) <= kFoldMaxParts &&
+           all_aligned16(w, g, m, v);
+}
+
+// a1 then a2 + a3 in one kernel. ev (optional, profiling): ev[0] / ev[1] take
+// the partial kernel's start / end, ev[2] / ev[3] the update's.
+int launch_step_fold(float *w, const float *g, float *m, float *v, int64_t n, float clip,
+                     const StepScalars &h, Workspace *ws, hipStream_t stream,
+                     hipEvent_t *ev = nullptr) {
+    launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+    const int64_t n4 = n >> 2;
+    int64_t blocks = (n4 + kUpdThreads - 1) / kUpdThreads;
+    if (blocks < 1) blocks = 1;
+    hipExtLaunchKernelGGL(adamw_update_vec_fold, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
+                          stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0,
+                          reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
+                          reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n,
+                          (const double *)ws->partials, norm_blocks(n), clip, ws->scalars, h);
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
@@ -533,7 +639,7 @@ int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *
 int launch_update(float *w, const float *g, float *m, float *v, int64_t n, const ClipScalars *sc,
                   const StepScalars &h, hipStream_t stream, hipEvent_t *ev = nullptr) {
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-    if (aligned16(w) && aligned16(g) && aligned16(m) && aligned16(v)) {
+    if (all_aligned16(w, g, m, v)) {
         const int64_t n4 = n >> 2;
         int64_t blocks = (n4 + kUpdChunk - 1) / kUpdChunk;
         if (blocks < 1) blocks = 1;
@@ -633,8 +739,12 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
         if (g_prof.on && (g_prof.calls++ % g_prof.every) == 0 && g_prof.next < g_prof.max_records)
             ev = &g_prof.ev[4 * g_prof.next++];
     }
-    if ((rc = launch_norm(g, n, grad_scale, clip, ws, stream, ev)) != RCS_OK) return rc;
-    rc = launch_update(w, g, m, v, n, ws->scalars, h, stream, ev ? ev + 2 : nullptr);
+    if (fold_final(w, g, m, v, n)) {
+        rc = launch_step_fold(w, g, m, v, n, clip, h, ws, stream, ev);
+    } else {
+        if ((rc = launch_norm(g, n, grad_scale, clip, ws, stream, ev)) != RCS_OK) return rc;
+        rc = launch_update(w, g, m, v, n, ws->scalars, h, stream, ev ? ev + 2 : nullptr);
+    }
     ws->has_norm = true;
     return rc;
 }

@@ -215,8 +215,31 @@ def test_update_parity_stress_subnormals_full_size(dev):
     assert sub.sum() > 0, "stress grads should leave subnormal first moments"
 
 
-def test_nonfinite_norm_skips_update(dev):
-    n = 10_000
+# Up to 256 norm partials (n <= 4,194,304, 16-byte aligned arrays) the update
+# kernel reduces the partials itself instead of a separate final kernel; its
+# reduction must give the final kernel's bits. grad_global_norm always runs
+# the final kernel, so the two norms of one gradient must be equal.
+@pytest.mark.parametrize("n", [4, 5, 4099, 262_147, 1_048_576, 4_194_304, 4_194_305, 4_194_308])
+def test_step_norm_same_bits_as_final_kernel(dev, n):
+    g = workloads.custom(140, n, 0.01, device=dev)
+    g[n // 2] = 3.0  # one large element: the step clips
+    w = workloads.custom(141, n, 0.02, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, og = _host(w).copy(), _host(g)
+    om, ov = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    standalone = float(rcs.grad_global_norm(g).cpu())
+    for t in (1, 2):
+        rcs.adamw_clip_step(w, g, m, v, t, 3e-3, 0.01, 1.0)
+        step = _gpu_norm()
+        assert np.float64(step).tobytes() == np.float64(standalone).tobytes(), (n, step, standalone)
+        rc, on = oracle.adamw_clip_step(ow, og, om, ov, t, 3e-3, 0.01, 1.0)
+        assert rc == oracle.OK and on > 1.0
+        assert abs(step - on) <= NORM_RTOL * on
+        _check_state(w, m, v, ow, om, ov, f"n={n} t={t}")
+
+
+@pytest.mark.parametrize("n", [10_000, 5_000_001])
+def test_nonfinite_norm_skips_update(dev, n):
     w = workloads.custom(104, n, 0.02, device=dev)
     m = workloads.custom(105, n, 0.01, device=dev)
     v = workloads.custom(106, n, 0.01, device=dev).abs_()
