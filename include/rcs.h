@@ -14,7 +14,8 @@
  * scalars). It is allocated by rcs_init or on the first call that needs it,
  * never inside a later call, and lives until the process ends. (The
  * asynchronous pack also keeps two HIP events per snapshot buffer, and the
- * instrumentation its events while enabled.)
+ * instrumentation its events while enabled. An rcs_ckpt_writer, created and
+ * destroyed explicitly, owns its snapshot, host buffer, stream and thread.)
  *
  * Every call validates its arguments on the host before enqueuing anything and
  * returns one of the status codes below; a negative return means nothing was
@@ -230,6 +231,36 @@ int ckpt_file_rotate(const char *dir, int keep);
 #define RCS_SIG_WRITE_EXIT 2
 int rcs_signals_install(void);
 int rcs_signals_poll(void);
+
+/*
+ * Asynchronous step-file writer (the sharded-resume lesson's production
+ * patterns: asynchronous, atomic, keep the newest K; the checkpoints page's
+ * SIGTERM save, after which the caller waits and exits). The writer owns a
+ * device snapshot (12 n bytes), a pinned host buffer (8 + 12 n bytes), a copy
+ * stream and one worker thread, all made by rcs_ckpt_writer_create on the
+ * current device and freed by rcs_ckpt_writer_destroy.
+ *
+ * rcs_ckpt_writer_submit: waits until the previous write has finished (if
+ * that write failed, returns its status and submits nothing), then enqueues
+ * ckpt_pack_async of (step, w, m, v) -- a snapshot kernel on compute_stream,
+ * the device-to-host copy on the writer's copy stream -- and returns; the
+ * worker waits for the copy, writes <dir>/step_%06d.bin atomically
+ * (ckpt_file_write) and keeps the `keep` newest files (ckpt_file_rotate).
+ * w, m, v may be updated by later work on compute_stream right away. Must be
+ * called with the writer's device current; submits are serialized.
+ * rcs_ckpt_writer_wait: blocks until no write is in flight and returns the
+ * status of the last finished one; path_out (optional, path_cap bytes)
+ * receives the path it wrote. Both are reported once: a second wait returns
+ * RCS_OK and "".
+ * rcs_ckpt_writer_destroy: waits, stops the worker, frees everything; returns
+ * the status of the last write not yet reported. NULL is a no-op.
+ */
+typedef struct rcs_ckpt_writer rcs_ckpt_writer;
+int rcs_ckpt_writer_create(const char *dir, int64_t n, int keep, rcs_ckpt_writer **out);
+int rcs_ckpt_writer_submit(rcs_ckpt_writer *writer, int32_t step, const float *w, const float *m,
+                           const float *v, hipStream_t compute_stream);
+int rcs_ckpt_writer_wait(rcs_ckpt_writer *writer, char *path_out, int64_t path_cap);
+int rcs_ckpt_writer_destroy(rcs_ckpt_writer *writer);
 
 /*
  * Instrumentation: while enabled, adamw_clip_step has its kernel dispatches

@@ -22,6 +22,7 @@ __all__ = [
     "RcsError", "adamw_clip_step", "adamw_clip_step_accum", "grad_clip_inplace", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
     "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read", "fp32_div_sqrt_probe",
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
+    "ckpt_pack_async", "ckpt_pack_wait", "CkptWriter", "StepFileCheckpointer",
 ]
 
 OK, EINVAL, ESIZE, EHEADER, EHIP, ENOMEM, EIO, ENOENT = 0, -1, -2, -3, -4, -5, -6, -7
@@ -101,6 +102,14 @@ def lib() -> ctypes.CDLL:
     L.rcs_signals_install.restype = ctypes.c_int
     L.rcs_signals_poll.argtypes = []
     L.rcs_signals_poll.restype = ctypes.c_int
+    L.rcs_ckpt_writer_create.argtypes = [cp, i64, ctypes.c_int, ctypes.POINTER(vp)]
+    L.rcs_ckpt_writer_create.restype = ctypes.c_int
+    L.rcs_ckpt_writer_submit.argtypes = [vp, i32, f32p, f32p, f32p, vp]
+    L.rcs_ckpt_writer_submit.restype = ctypes.c_int
+    L.rcs_ckpt_writer_wait.argtypes = [vp, ctypes.c_char_p, i64]
+    L.rcs_ckpt_writer_wait.restype = ctypes.c_int
+    L.rcs_ckpt_writer_destroy.argtypes = [vp]
+    L.rcs_ckpt_writer_destroy.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -309,6 +318,49 @@ def signals_poll() -> int:
     return lib().rcs_signals_poll()
 
 
+class CkptWriter:
+    """The library's asynchronous step-file writer (rcs_ckpt_writer_*): it owns
+    a device snapshot, a pinned host buffer, a copy stream and a worker thread
+    that writes <dir>/step_NNNNNN.bin atomically and keeps the newest `keep`."""
+
+    def __init__(self, directory, n: int, keep: int = 3):
+        os.makedirs(directory, exist_ok=True)
+        h = ctypes.c_void_p()
+        _check(lib().rcs_ckpt_writer_create(_b(directory), int(n), int(keep), ctypes.byref(h)),
+               "rcs_ckpt_writer_create")
+        self._h, self.n = h, int(n)
+
+    def submit(self, step: int, w, m, v, stream=None) -> None:
+        """Snapshot of (w, m, v) on the stream, then copy and write in the
+        background; raises first if the previous write failed."""
+        if self._h is None:
+            raise ValueError("writer is closed")
+        n = self.n
+        ptrs = (_dev_f32(w, "w", n), _dev_f32(m, "m", n), _dev_f32(v, "v", n))
+        _check(lib().rcs_ckpt_writer_submit(self._h, int(step), *ptrs, _stream(stream)),
+               "rcs_ckpt_writer_submit")
+
+    def wait(self) -> str:
+        """Waits for the write in flight; returns the path written since the
+        last wait ("" if none) or raises its error."""
+        if self._h is None:
+            return ""
+        out = ctypes.create_string_buffer(4096)
+        _check(lib().rcs_ckpt_writer_wait(self._h, out, 4096), "rcs_ckpt_writer_wait")
+        return os.fsdecode(out.value)
+
+    def close(self) -> None:
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(lib().rcs_ckpt_writer_destroy(h), "rcs_ckpt_writer_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class StepFileCheckpointer:
     """Step-file policy around a training loop: call after_step(t, w, m, v)
     after every completed update. It writes <dir>/step_NNNNNN.bin when t is a
@@ -317,65 +369,48 @@ class StepFileCheckpointer:
     the caller exits), keeps the newest `keep` files, and resume() loads the
     newest valid one.
 
-    async_write=True takes the state with ckpt_pack_async (a device snapshot on
-    the training stream, drained on a copy stream) and writes the file from a
-    background thread, so training continues during both the host-link copy
-    and the disk write; the next save, a SIGTERM save and flush() wait for the
-    previous write first."""
+    async_write=True hands each save to the library's CkptWriter (a device
+    snapshot on the training stream, the copy on its own stream, the atomic
+    write and rotation on its worker thread), so training continues during
+    both the host-link copy and the disk write; the next save, a SIGTERM save
+    and flush() wait for the previous write first."""
 
     def __init__(self, directory, n: int, every: int = 100, keep: int = 3,
                  install_signals: bool = True, stream=None, async_write: bool = False):
-        import threading
-
         self.dir, self.n, self.every, self.keep = directory, int(n), int(every), int(keep)
         os.makedirs(directory, exist_ok=True)
-        self.buf = torch.empty(ckpt_bytes(self.n), dtype=torch.uint8, pin_memory=True)
         self.stream = stream
         self.written: list[str] = []
         self.async_write = bool(async_write)
-        self._thread: "threading.Thread | None" = None
-        self._error: BaseException | None = None
-        if self.async_write:
-            self.snapshot = torch.empty(ckpt_snapshot_bytes(self.n) // 4, dtype=torch.float32,
-                                        device="cuda")
-            self.copy_stream = torch.cuda.Stream()
+        self.buf = torch.empty(ckpt_bytes(self.n), dtype=torch.uint8, pin_memory=True)
+        self._writer = CkptWriter(directory, self.n, self.keep) if self.async_write else None
         if install_signals:
             signals_install()
 
-    def _finish(self) -> None:
-        path = ckpt_file_write(self.dir, self.buf)
-        self.written.append(path)
-        ckpt_file_rotate(self.dir, self.keep)
-
-    def _background(self) -> None:
-        try:
-            ckpt_pack_wait(self.snapshot)
-            self._finish()
-        except BaseException as e:  # surfaced by flush()
-            self._error = e
-
     def flush(self) -> None:
-        """Waits for an asynchronous write in flight and re-raises its error."""
-        if self._thread is not None:
-            self._thread.join()
-            self._thread = None
-        if self._error is not None:
-            e, self._error = self._error, None
-            raise e
+        """Waits for an asynchronous write in flight and raises its error."""
+        if self._writer is not None:
+            path = self._writer.wait()
+            if path:
+                self.written.append(path)
+
+    def close(self) -> None:
+        """flush(), then frees the asynchronous writer."""
+        self.flush()
+        if self._writer is not None:
+            self._writer.close()
+            self._writer = None
+            self.async_write = False
 
     def save(self, t: int, w, m, v, wait: bool = False) -> None:
         self.flush()
-        if not self.async_write:
+        if self._writer is None:
             ckpt_pack(t, w, m, v, self.buf, stream=self.stream)
             torch.cuda.synchronize()
-            self._finish()
+            self.written.append(ckpt_file_write(self.dir, self.buf))
+            ckpt_file_rotate(self.dir, self.keep)
             return
-        import threading
-
-        ckpt_pack_async(t, w, m, v, self.snapshot, self.buf, compute_stream=self.stream,
-                        copy_stream=self.copy_stream)
-        self._thread = threading.Thread(target=self._background, daemon=True)
-        self._thread.start()
+        self._writer.submit(t, w, m, v, stream=self.stream)
         if wait:
             self.flush()
 

@@ -8,6 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "rcs.hip")
 SRC_IO = os.path.join(PKG, "csrc", "ckpt_io.cpp")
+SRC_WRITER = os.path.join(PKG, "csrc", "ckpt_writer.cpp")
 LIB = os.path.join(PKG, "librcs.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -31,7 +32,7 @@ def hipcc() -> str:
 def build(extra_flags: list[str] | None = None, out: str | None = None) -> str:
     out = out or LIB
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, SRC_IO, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, SRC_IO, SRC_WRITER, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag and says so
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"

@@ -487,6 +487,12 @@ __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restr
 
 // ---------------------------------------------------------------- host side
 
+}  // namespace
+
+#include "rcs_internal.h"
+
+namespace {
+
 struct Workspace {
     double *partials = nullptr;      // kNormMaxBlocks float64
     ClipScalars *scalars = nullptr;  // one record
@@ -670,6 +676,15 @@ int32_t get_le32(const unsigned char *p) {
 bool valid_n(int64_t n) { return n >= 1 && n <= RCS_MAX_N; }
 
 }  // namespace
+
+void rcs_snapshot_forget(int dev, const void *snapshot) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_snap.find(std::make_pair(dev, snapshot));
+    if (it == g_snap.end()) return;
+    (void)hipEventDestroy(it->second.ready);
+    (void)hipEventDestroy(it->second.copied);
+    g_snap.erase(it);
+}
 
 // ---------------------------------------------------------------- C ABI
 

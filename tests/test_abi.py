@@ -123,6 +123,19 @@ def test_unpack_header_faults_rejected_before_any_copy(L, case, want):
     assert step.value == -7
 
 
+def test_writer_argument_rejections_need_no_device(L):
+    import ctypes
+    h = ctypes.c_void_p()
+    assert L.rcs_ckpt_writer_create(None, 10, 1, ctypes.byref(h)) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_create(b"/tmp", 0, 1, ctypes.byref(h)) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_create(b"/tmp", rcs.MAX_N + 1, 1, ctypes.byref(h)) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_create(b"/tmp", 10, 0, ctypes.byref(h)) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_create(b"/tmp", 10, 1, None) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_submit(None, 1, None, None, None, None) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_wait(None, None, 0) == rcs.EINVAL
+    assert L.rcs_ckpt_writer_destroy(None) == rcs.OK
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     a = torch.zeros(8)

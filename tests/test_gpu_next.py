@@ -1,6 +1,7 @@
 """GPU tests of the rows built on top of the hot path: micro-batch
-accumulation folded into the kernels, the asynchronous snapshot pack, and
-signal-driven step files with resume."""
+accumulation folded into the kernels, the asynchronous snapshot pack, the
+library's asynchronous step-file writer, and signal-driven step files with
+resume."""
 import os
 import subprocess
 import sys
@@ -108,6 +109,61 @@ def _unpacked(buf, n):
     raw = buf.numpy()
     return [torch.from_numpy(raw[8 + 4 * j * n: 8 + 4 * (j + 1) * n].view(np.float32).copy())
             for j in range(3)]
+
+
+@pytest.mark.parametrize("n", [262_147, 1_000_000])
+def test_native_writer_files_are_the_state_at_submit(dev, tmp_path, n):
+    """The library's writer: each submit snapshots the state on the training
+    stream while later updates go on; every file equals a synchronous pack
+    taken at its step, keep=2 leaves the two newest, and a second wait
+    reports nothing new."""
+    wl = workloads.WORKLOADS["flat262k"]
+    w = workloads.init_params(wl, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    g = torch.empty(n, device=dev)
+    wr = rcs.CkptWriter(tmp_path, n, keep=2)
+    ref, written = {}, []
+    for t in range(1, 26):
+        workloads.grads(wl, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        if t % 5 == 0:
+            ref[t] = torch.empty(rcs.ckpt_bytes(n), dtype=torch.uint8, pin_memory=True)
+            rcs.ckpt_pack(t, w, m, v, ref[t])
+            if t > 5:
+                written.append(wr.wait())
+            wr.submit(t, w, m, v)
+    written.append(wr.wait())
+    assert wr.wait() == ""
+    torch.cuda.synchronize()
+    assert [os.path.basename(p) for p in written] == [rcs.step_file_name(t) for t in ref]
+    assert sorted(os.listdir(tmp_path)) == ["step_000020.bin", "step_000025.bin"]
+    for t in (20, 25):
+        assert open(tmp_path / rcs.step_file_name(t), "rb").read() == ref[t].numpy().tobytes()
+    wr.close()
+
+
+def test_native_writer_reports_a_failed_write(dev, tmp_path):
+    n = 4099
+    w = workloads.custom(300, n, 0.02, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    d = tmp_path / "ckpt"
+    wr = rcs.CkptWriter(d, n, keep=1)
+    os.rmdir(d)  # the directory is gone: the worker's write fails
+    wr.submit(1, w, m, v)
+    with pytest.raises(rcs.RcsError) as e:
+        wr.wait()
+    assert e.value.status == rcs.EIO
+    assert wr.wait() == ""  # reported once
+    wr.submit(2, w, m, v)  # fails in the background again ...
+    with pytest.raises(rcs.RcsError) as e:
+        wr.submit(3, w, m, v)  # ... and the next submit reports it, submitting nothing
+    assert e.value.status == rcs.EIO
+    os.makedirs(d)
+    wr.submit(4, w, m, v)
+    assert os.path.basename(wr.wait()) == "step_000004.bin"
+    assert os.listdir(d) == ["step_000004.bin"]
+    wr.close()
+    wr.close()  # idempotent
 
 
 @pytest.mark.parametrize("mode", ["sync", "async"])
