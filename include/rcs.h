@@ -238,7 +238,9 @@ int rcs_signals_poll(void);
  * SIGTERM save, after which the caller waits and exits). The writer owns a
  * device snapshot (12 n bytes), a pinned host buffer (8 + 12 n bytes), a copy
  * stream and one worker thread, all made by rcs_ckpt_writer_create on the
- * current device and freed by rcs_ckpt_writer_destroy.
+ * current device and freed by rcs_ckpt_writer_destroy. dir must exist (as
+ * for ckpt_file_write); a missing or unwritable one makes each write fail
+ * with RCS_EIO.
  *
  * rcs_ckpt_writer_submit: waits until the previous write has finished (if
  * that write failed, returns its status and submits nothing), then enqueues

@@ -1,6 +1,8 @@
-"""Native callers of the library, built here with the host compilers:
-include/rcs.h compiles as C and a C program links and calls librcs.so; the
-host file-IO code runs under AddressSanitizer and UndefinedBehaviorSanitizer
+"""Native callers of the library, built with the host compilers:
+include/rcs.h compiles as C and a C program links and calls librcs.so (host
+rejections here; a whole C training loop with pack, file write and the
+asynchronous writer on the GPU, checked against the oracle); the host
+file-IO code runs under AddressSanitizer and UndefinedBehaviorSanitizer
 (host code only: no device code is built with a sanitizer)."""
 import os
 import shutil
@@ -59,3 +61,61 @@ def test_oracle_under_address_and_ub_sanitizers(tmp_path):
           "-lm", "-o", str(exe)])
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
     assert "oracle driver ok" in _run([str(exe)], env=env)
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+@pytest.mark.parametrize("n", [100_003, 5_000_001])
+def test_c_program_trains_and_saves_on_the_gpu(tmp_path, n):
+    """A C program drives three updates, the pack, the step-file write and the
+    asynchronous writer through the C ABI alone; its norms and its file match
+    the oracle run on the same inputs (n = 100,003 takes the two-launch step,
+    5,000,001 the three-launch one; both have a ragged tail)."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    from util import max_ulp
+
+    exe = tmp_path / "c_step_driver"
+    libdir = os.path.dirname(rcs.LIB_PATH)
+    _run(["gcc", "-std=c11", "-Wall", "-Werror", *HIP_DEFS, os.path.join(NATIVE, "c_step_driver.c"),
+          f"-L{libdir}", "-l:librcs.so", f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{libdir}",
+          f"-Wl,-rpath,{ROCM}/lib", "-o", str(exe)])
+    steps, lr, wd, clip = 3, 3e-3, 0.01, 1.0
+    w0 = workloads.custom(310, n, 0.02).numpy()
+    gs = [workloads.custom(311 + t, n, sigma).numpy() for t, sigma in enumerate((1e-3, 1e-2, 2e-3))]
+    inp = tmp_path / "in.bin"
+    with open(inp, "wb") as f:
+        for a in (w0, *gs):
+            f.write(a.astype("<f4").tobytes())
+    d1, d2 = tmp_path / "file", tmp_path / "writer"
+    d1.mkdir()
+    d2.mkdir()
+    out = _run([str(exe), str(inp), str(n), str(steps), repr(lr), repr(wd), repr(clip), str(d1),
+                str(d2)], timeout=120)
+    assert "c step driver ok" in out
+    norms, paths = {}, {}
+    for ln in out.splitlines():
+        key, _, rest = ln.partition(" ")
+        if key == "norm":
+            t, x = rest.split()
+            norms[int(t)] = float(x)
+        elif key in ("file", "writer"):
+            paths[key] = rest
+    ow, om, ov = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, steps + 1):
+        rc, on = oracle.adamw_clip_step(ow, gs[t - 1], om, ov, t, lr, wd, clip)
+        assert rc == oracle.OK
+        gn = norms[t]
+        assert abs(gn - on) <= 1e-12 * on, (t, gn, on)
+    raw = open(paths["file"], "rb").read()
+    assert os.path.basename(paths["file"]) == "step_000003.bin"
+    _, expect = oracle.ckpt_pack(steps, ow, om, ov)
+    assert raw[:8] == expect.tobytes()[:8]
+    got = np.frombuffer(raw, dtype=np.uint8)
+    for j, ref in enumerate((ow, om, ov)):
+        arr = got[8 + 4 * j * n: 8 + 4 * (j + 1) * n].view(np.float32)
+        assert max_ulp(arr, ref) <= 2, j
+    assert os.path.basename(paths["writer"]) == "step_000003.bin"
+    assert open(paths["writer"], "rb").read() == raw
