@@ -201,6 +201,64 @@ def copy_calibration(gib: float, reps: int) -> None:
                       "reps": reps}))
 
 
+def torch_reference(torch, wl, w, grads, steps: int) -> dict:
+    """PyTorch's own fused AdamW after its global-norm clip, on one float32
+    parameter of the same size with the same gradients, timed the same way on
+    the current stream: a speed reference on the same GPU, not a parity one
+    (its clip adds 1e-6 to the norm and its AdamW orders the float32 work
+    differently)."""
+    p = torch.nn.Parameter(w.detach().clone())
+    opt = torch.optim.AdamW([p], lr=wl.lr, betas=(0.9, 0.999), eps=1e-8,
+                            weight_decay=wl.wd, fused=True)
+    k = 0
+
+    def step():
+        nonlocal k
+        p.grad = grads[k % len(grads)]
+        k += 1
+        torch.nn.utils.clip_grad_norm_([p], wl.clip, foreach=True)
+        opt.step()
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    del opt, p
+    torch.cuda.empty_cache()
+
+    # PyTorch's own streaming kernels on float32[n] buffers, for the roofline's
+    # context: read/written bytes over time, GB/s
+    a, b = grads[0], grads[1]
+    c, d = torch.empty_like(a), torch.empty_like(a)
+    nb = 4 * a.numel()
+    ops = {"copy_1r1w": (lambda: c.copy_(a), 2 * nb),
+           "add_2r1w": (lambda: torch.add(a, b, out=c), 3 * nb),
+           "addcmul_3r1w": (lambda: torch.addcmul(a, b, c, out=d), 4 * nb),
+           "sum_1r": (lambda: a.sum(), nb)}
+    streaming = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(3):
+            fn()
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        streaming[name] = nbytes / (e0.elapsed_time(e1) / 20 / 1e3) / 1e9
+    del c, d
+    torch.cuda.empty_cache()
+    return {"us_per_step": us, "params_per_s": w.numel() / us * 1e6, "steps": steps,
+            "what": "torch.nn.utils.clip_grad_norm_(foreach=True) + "
+                    "torch.optim.AdamW(fused=True), float32, same n and gradients",
+            "streaming_GBps": streaming}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +268,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-ckpt", action="store_true", help="skip the pack/unpack leg")
+    ap.add_argument("--no-torch-ref", action="store_true",
+                    help="skip timing PyTorch's fused AdamW + clip on the same inputs")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -342,6 +402,11 @@ def main() -> int:
     torch.cuda.synchronize()
     clip_s = ev0.elapsed_time(ev1) / reps / 1e3
     result["grad_clip_inplace"] = {"us": clip_s * 1e6, "GBps_12B_per_param": 12 * n / clip_s / 1e9}
+
+    if not args.no_torch_ref:
+        ref = torch_reference(torch, wl, w, grads, min(args.steps, 50))
+        ref["our_speedup"] = ref["us_per_step"] / (ms_step * 1e3)
+        result["torch_reference"] = ref
 
     if not args.no_ckpt:
         nb = rcs.ckpt_bytes(n)
