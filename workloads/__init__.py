@@ -94,7 +94,8 @@ WORKLOADS: dict[str, Workload] = {
                  "12.8M flat; grads N(0,1e-4), 1% x100 only on steps t%3==0 (clip fires "
                  "on those steps only)"),
         Workload(3, "andrea120m", ANDREA120M_N, 100, 3e-3, 0.01, 1.0, 1e-4, "andrea120m",
-                 "normal", (), "ANDREA-120M layout, 124,356,864 params; grads N(0,1e-4)"),
+                 "normal", (), "ANDREA-120M layout, 124,356,864 params (matrices N(0,0.02), "
+                 "LayerNorm gains 1 and biases 0); grads N(0,1e-4)"),
         Workload(4, "andrea120m_stress", ANDREA120M_N, 200, 3e-3, 0.01, 1.0, 1.0, "andrea120m",
                  "stress", (100,), "ANDREA-120M layout; grads N(0,1), 5% exact zeros, 0.1% "
                  "+-U[0.5,2]e-38 (subnormal and near FLT_MIN)"),
