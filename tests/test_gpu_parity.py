@@ -518,6 +518,44 @@ def test_edge_scalars_and_values(dev, case):
         assert (_host(w) == _host(workloads.custom(400, n, 0.02, device=dev))).all()
 
 
+def test_randomized_cases_against_oracle(dev):
+    """160 seeded random cases, two updates each: sizes 1 .. ~70,000 (both
+    launch forms, ragged tails), unaligned views (scalar kernels), t up to
+    2^31 - 2, lr, wd, clip and gradient scales over many decades (clipped and
+    unclipped), micro-batch scales; the norm and w, m, v against the oracle at
+    the usual bar."""
+    rng = np.random.default_rng(20240607)
+    clipped = unclipped = 0
+    for case in range(160):
+        n = int(np.exp(rng.uniform(0.0, np.log(70_000))))
+        off = int(rng.choice([0, 0, 1, 2, 3]))
+        t = int(min(np.exp(rng.uniform(0.0, np.log(2**31 - 2))), 2**31 - 2))
+        lr = float(10 ** rng.uniform(-6, -1))
+        wd = float(rng.choice([0.0, rng.uniform(0.0, 0.2)]))
+        clip = float("inf") if rng.random() < 0.1 else float(10 ** rng.uniform(-3, 2))
+        sigma = float(10 ** rng.uniform(-8, 1))
+        scale = float(np.float32(1.0) / np.float32(rng.choice([1, 2, 3, 4, 7])))
+        base = 1000 + 4 * case
+        arrs = []
+        for k, sd in enumerate((0.02, sigma, 0.01, 0.01)):
+            x = workloads.custom(base + k, n + off, sd, device=dev)[off:]
+            arrs.append(x.square_() if k == 3 else x)
+        w, g, m, v = arrs
+        ow, og, om, ov = (_host(x).copy() for x in arrs)
+        ctx = f"case {case}: n={n} off={off} t={t} lr={lr:.3g} wd={wd:.3g} clip={clip:.3g} " \
+              f"sigma={sigma:.3g} scale={scale:.3g}"
+        for tt in (t, t + 1):
+            rcs.adamw_clip_step_accum(w, g, m, v, tt, lr, wd, clip, scale)
+            gn = _gpu_norm()
+            rc, on = oracle.adamw_clip_step_accum(ow, og, om, ov, tt, lr, wd, clip, scale)
+            assert rc == oracle.OK, ctx
+            assert abs(gn - on) <= NORM_RTOL * on, (ctx, gn, on)
+            _check_state(w, m, v, ow, om, ov, ctx)
+        clipped += on > clip
+        unclipped += on <= clip
+    assert clipped > 20 and unclipped > 20, (clipped, unclipped)
+
+
 def test_two_streams_have_separate_workspaces(dev):
     """Two parameter sets updated concurrently on two streams: each stream has
     its own partials and clip scalars, so both match the oracle and each
