@@ -382,10 +382,18 @@ class StepFileCheckpointer:
         self.stream = stream
         self.written: list[str] = []
         self.async_write = bool(async_write)
-        self.buf = torch.empty(ckpt_bytes(self.n), dtype=torch.uint8, pin_memory=True)
+        self._buf: torch.Tensor | None = None  # pinned host image, made on first use
         self._writer = CkptWriter(directory, self.n, self.keep) if self.async_write else None
         if install_signals:
             signals_install()
+
+    @property
+    def buf(self) -> torch.Tensor:
+        """Pinned host image of a step file (synchronous saves and resume; the
+        asynchronous writer has its own)."""
+        if self._buf is None:
+            self._buf = torch.empty(ckpt_bytes(self.n), dtype=torch.uint8, pin_memory=True)
+        return self._buf
 
     def flush(self) -> None:
         """Waits for an asynchronous write in flight and raises its error."""
