@@ -10,7 +10,7 @@
  * caller must not touch the arrays or host buffers before then.
  *
  * The only device memory the library owns is a per-(device, stream)
- * workspace of about 17 KiB (2048 per-block float64 partial sums and the clip
+ * workspace of about 2.3 KiB (256 per-block float64 partial sums and the clip
  * scalars). It is allocated by rcs_init or on the first call that needs it,
  * never inside a later call, and lives until the process ends. (The
  * asynchronous pack also keeps two HIP events per snapshot buffer, and the
@@ -84,10 +84,11 @@ int rcs_init(int device, hipStream_t stream);
  * If the norm is not finite the update is skipped on the device (w, m, v are
  * left untouched); read the norm with last_grad_norm.
  * The reduction order depends only on n, so results are deterministic.
- * 16-byte aligned arrays take the vector path; others a scalar path with the
- * same arithmetic. With aligned arrays and 4 <= n <= 4,194,304 the final
- * reduction runs inside the update kernel (two launches instead of three;
- * same reduction order, so the same norm bits as grad_global_norm).
+ * With 16-byte aligned arrays and n >= 4 the step is two launches (the
+ * partial sums, then the update kernel, which does the final reduction in
+ * grad_norm_final's order: the same norm bits as grad_global_norm); other
+ * arrays take partial, final and a scalar update kernel with the same
+ * arithmetic.
  */
 int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                     float lr, float wd, float clip, hipStream_t stream);
@@ -266,9 +267,10 @@ int rcs_ckpt_writer_destroy(rcs_ckpt_writer *writer);
 
 /*
  * Instrumentation: while enabled, adamw_clip_step has its kernel dispatches
- * stamp HIP events (start of grad_norm_partial, end of grad_norm_final -- or
- * of grad_norm_partial when the update kernel does the final reduction --,
- * start and end of the update kernel) on one call in `every` (the first call after
+ * stamp HIP events (start of grad_norm_partial, end of the last norm kernel
+ * -- grad_norm_partial itself when the update kernel does the final
+ * reduction --, start and end of the update kernel) on one call in `every`
+ * (the first call after
  * enabling is recorded), up to max_records recorded calls. rcs_profile_read synchronizes those events and returns the
  * summed milliseconds and the number of recorded calls. Enabling (or
  * disabling) discards earlier records. Events are created here, not in the

@@ -14,31 +14,28 @@
 //     region" and "Total size": [int32 step][int32 n][w][m][v], 8 + 12 n bytes.
 //
 // Hardware mapping (MI355X, CDNA4, 64-wide waves, 256 CUs):
-//   * grad_norm_partial: a grid fixed by n alone streams g with 16-byte
-//     loads, squares in float64 (exact for float32 inputs) into four
-//     independent accumulators per lane, reduces each wave with DPP row
-//     permutes plus two cross-row swizzles, and combines the block's waves
-//     through LDS in wave order: one float64 partial per block. The last
-//     320 MB of g are read with cache-allocating loads so that the part of g
-//     still in the 256 MB last-level cache serves the update's second read;
-//     the rest streams.
-//   * grad_norm_final: one 1024-lane block sums the partials in a fixed tree,
-//     takes the float64 square root and writes {norm, clip factor, apply
-//     flag}. No floating-point atomics anywhere, so the result depends only
-//     on n and the data. (A single kernel whose last block does this step
-//     needs a device-scope release per block, which on this chip costs an L2
-//     write-back per block and measured slower than the extra launch.)
-//   * adamw_update_vec: pure HBM stream (16 B read + 12 B written per element)
-//     with 16-byte streaming loads/stores of w, g, m, v, one vector of each per
-//     lane; each XCD streams its own contiguous eighth of the vectors (block b
-//     works in region b % 8, blocks being dispatched round-robin over the 8
-//     XCDs), which evens out DRAM contention between the seven streams. The
-//     clip factor is read from device memory, so the host never waits between
-//     kernels.
-//   * adamw_update_vec_fold: for small n (at most 256 partials) the update
-//     kernel does grad_norm_final's reduction at its head, so the step costs
-//     two launches, not three; below a few million elements the step is bound
-//     by the runtime's per-launch host cost, not by HBM.
+//   * grad_norm_partial: a grid fixed by n alone (at most 256 blocks of 512
+//     lanes) streams g with 16-byte loads, squares in float64 (exact for
+//     float32 inputs) into four independent accumulators per lane, reduces
+//     each wave with DPP row permutes plus two cross-row swizzles, and
+//     combines the block's waves through LDS in wave order: one float64
+//     partial per block. The last 320 MB of g are read with cache-allocating
+//     loads so that the part of g still in the 256 MB last-level cache serves
+//     the update's second read; the rest streams.
+//   * adamw_update_vec: each block first sums the <= 256 partials in a fixed
+//     tree (grad_norm_final's step, folded in: one launch and one kernel
+//     boundary fewer per step), takes the float64 square root and the clip
+//     factor, then streams one 16-byte vector of w, g, m, v per lane (16 B read
+//     + 12 B written per element) with streaming loads and stores. Each XCD
+//     streams its own contiguous eighth of the vectors (block b works in
+//     region b % 8, blocks being dispatched round-robin over the 8 XCDs),
+//     which evens out DRAM contention between the seven streams. No float
+//     atomics anywhere, so the result depends only on n and the data. (A
+//     single kernel whose last block does the final step needs a device-scope
+//     release per block, which on this chip costs an L2 write-back per block
+//     and measured slower.)
+//   * grad_norm_final: the same final step as a kernel of its own, for the
+//     norm alone, the in-place clip and the scalar (unaligned) update.
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -63,12 +60,6 @@
 #pragma clang fp contract(off)
 
 // Launch-shape knobs (overridable at build time for sweeps).
-#ifndef RCS_UPD_THREADS
-#define RCS_UPD_THREADS 256
-#endif
-#ifndef RCS_UPD_UNROLL
-#define RCS_UPD_UNROLL 1
-#endif
 // Contiguous regions of the vectors the update streams at once: block b
 // works in region b % k. Blocks are dispatched round-robin over the chip's 8
 // XCDs, so with k = 8 each XCD streams its own contiguous eighth of w, g, m, v.
@@ -79,12 +70,6 @@
 #endif
 #ifndef RCS_UPD_NT
 #define RCS_UPD_NT 1
-#endif
-// Steps whose norm pass has at most 256 partials (n <= 4,194,304) and whose
-// arrays are 16-byte aligned fold the final reduction into the update kernel:
-// two launches instead of three. 0 keeps three launches at every size.
-#ifndef RCS_FOLD_FINAL
-#define RCS_FOLD_FINAL 1
 #endif
 // Bytes at the end of g that the norm pass reads with ordinary (cache-
 // allocating) loads so that the update, which reads g again right after,
@@ -97,14 +82,18 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kNormThreads = 256;
-constexpr int kNormUnroll = 4;  // 16-byte loads in flight per lane per iteration
+// Norm pass: at most 256 blocks of 512 lanes, 4 loads of 16 B in flight per
+// lane (measured best of 256-1024 lanes x 2-8 loads with 256 blocks, and of
+// the earlier 2048 blocks x 256 lanes with a separate final kernel).
+constexpr int kNormThreads = 512;
+constexpr int kNormUnroll = 4;
 constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormUnroll;  // vectors per block-iteration
-constexpr int kNormMaxBlocks = 2048;
-constexpr int kFinalThreads = 1024;
-constexpr int kUpdThreads = RCS_UPD_THREADS;
-constexpr int kUpdUnroll = RCS_UPD_UNROLL;
-constexpr int64_t kUpdChunk = (int64_t)kUpdThreads * kUpdUnroll;
+constexpr int kNormMaxBlocks = 256;
+// The final reduction (grad_norm_final, and the head of the update kernel)
+// gives lane i partial i; both use blocks of this many lanes.
+constexpr int kParts = 256;
+constexpr int kUpdThreads = kParts;  // update: one 16-byte vector of each array per lane
+static_assert(kNormMaxBlocks <= kParts, "one partial per lane in the final reduction");
 
 // Native 16-byte vector (the nontemporal builtins need a clang vector type).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -219,26 +208,27 @@ __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *_
     if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
-// a2: one block sums the partials (lane i takes partials i and i + 1024, then
-// the fixed wave/LDS tree), takes the float64 square root and writes
-// {norm, clip factor, apply flag}.
-static_assert(kNormMaxBlocks <= 2 * kFinalThreads, "final kernel reads two partials per lane");
-__global__ __launch_bounds__(kFinalThreads) void grad_norm_final(const double *__restrict__ partials,
-                                                                 int nparts, float clip,
-                                                                 ClipScalars *__restrict__ out) {
-    __shared__ double lds[kFinalThreads / kWave];
-    const int i0 = threadIdx.x, i1 = threadIdx.x + kFinalThreads;
-    const double x0 = (i0 < nparts) ? partials[i0] : 0.0;
-    const double x1 = (i1 < nparts) ? partials[i1] : 0.0;
-    const double S = block_sum<kFinalThreads>(x0 + x1, lds);
-    if (threadIdx.x == 0) {
-        const double norm = sqrt(S);
-        ClipScalars r;
-        r.norm = norm;
-        r.apply = isfinite(norm) ? 1 : 0;
-        r.scale = (norm > (double)clip) ? (float)((double)clip / norm) : 1.0f;
-        *out = r;
-    }
+// a2 as a device function: lane i of a kParts-lane block holds partial i (0
+// beyond nparts); the fixed wave/LDS tree sums them, then thread 0 takes the
+// float64 square root and the clip factor. The result is valid in thread 0.
+__device__ __forceinline__ ClipScalars final_reduce(double x, float clip, double *lds) {
+    const double S = block_sum<kParts>(x, lds);
+    ClipScalars r;
+    r.norm = sqrt(S);
+    r.apply = isfinite(r.norm) ? 1 : 0;
+    r.scale = (r.norm > (double)clip) ? (float)((double)clip / r.norm) : 1.0f;
+    return r;
+}
+
+// a2 as its own kernel (the norm alone, the in-place clip, and the scalar
+// update path): one kParts-lane block writes {norm, clip factor, apply flag}.
+__global__ __launch_bounds__(kParts) void grad_norm_final(const double *__restrict__ partials,
+                                                          int nparts, float clip,
+                                                          ClipScalars *__restrict__ out) {
+    __shared__ double lds[kParts / kWave];
+    const double x = ((int)threadIdx.x < nparts) ? partials[threadIdx.x] : 0.0;
+    const ClipScalars r = final_reduce(x, clip, lds);
+    if (threadIdx.x == 0) *out = r;
 }
 
 // ---------------------------------------------------------------- update
@@ -288,78 +278,30 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 #endif
 }
 
-// a3: fused clip-scale + AdamW, 16-byte vectors of w, g, m, v.
+// a2 + a3: every block first reduces the norm partials (the final kernel's
+// tree, so the same bits), then applies the clip factor and AdamW to one
+// 16-byte vector of w, g, m, v per lane, with streaming loads and stores;
+// block 0 also stores the record last_grad_norm reads. Folding a2 in saves a
+// launch and a kernel boundary per step; the 2 KB of partials each block reads
+// come from L2. The partial is loaded first and every load is unconditional
+// (lanes past the end re-read the last partial / vector and discard it; the
+// host guarantees n >= 4), so waiting for the partial leaves the four element
+// loads in flight during the reduction.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
-    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, const ClipScalars *__restrict__ sc, StepScalars h) {
-    if (!sc->apply) return;
-    const float s = sc->scale;
-    const int64_t n4 = n >> 2;
-    const int64_t nblk = gridDim.x;
-    int64_t c = blockIdx.x;
-    if (RCS_UPD_REGIONS > 1) {  // bijection of [0, nblk): region b % k, position b / k
-        const int64_t k = RCS_UPD_REGIONS, q = nblk / k, r = nblk % k, x = c % k, i = c / k;
-        c = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-    }
-    for (int64_t base = c * kUpdChunk; base < n4; base += nblk * kUpdChunk) {
-        f32x4 wr[kUpdUnroll], gr[kUpdUnroll], mr[kUpdUnroll], vr[kUpdUnroll];
-#pragma unroll
-        for (int j = 0; j < kUpdUnroll; ++j) {
-            const int64_t i = base + (int64_t)j * kUpdThreads + threadIdx.x;
-            if (i < n4) {
-                gr[j] = ld_stream(g + i);
-                wr[j] = ld_stream(w + i);
-                mr[j] = ld_stream(m + i);
-                vr[j] = ld_stream(v + i);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kUpdUnroll; ++j) {
-            const int64_t i = base + (int64_t)j * kUpdThreads + threadIdx.x;
-            if (i < n4) {
-                adamw_vec4(wr[j], gr[j], mr[j], vr[j], s, h);
-                st_stream(w + i, wr[j]);
-                st_stream(m + i, mr[j]);
-                st_stream(v + i, vr[j]);
-            }
-        }
-    }
-    // the n % 4 trailing elements
-    const int rem = (int)(n & 3);
-    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
-        const int64_t i = (n4 << 2) + threadIdx.x;
-        float *wf = reinterpret_cast<float *>(w);
-        float *mf = reinterpret_cast<float *>(m);
-        float *vf = reinterpret_cast<float *>(v);
-        const float *gf = reinterpret_cast<const float *>(g);
-        float ww = wf[i], mm = mf[i], vv = vf[i];
-        adamw_elem(ww, gf[i], mm, vv, s, h);
-        wf[i] = ww;
-        mf[i] = mm;
-        vf[i] = vv;
-    }
-}
-
-// a2 + a3 for small n (at most kFoldMaxParts partials): every block reduces the
-// partials itself, so the step is two launches instead of three. Lane i takes
-// partial i (0 beyond nparts) and the block sums in the same wave/LDS order as
-// grad_norm_final, whose extra lanes and waves only add +0.0 to a
-// non-negative sum: norm, clip factor and flag are the same bits. Block 0
-// also stores the record for last_grad_norm. The element loads are in flight
-// while the block reduces.
-constexpr int kFoldMaxParts = kUpdThreads;
-__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
     f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
     f32x4 *__restrict__ v, int64_t n, const double *__restrict__ partials, int nparts, float clip,
     ClipScalars *__restrict__ sc_out, StepScalars h) {
-    __shared__ double lds[kUpdThreads / kWave];
+    __shared__ double lds[kParts / kWave];
     __shared__ float s_scale;
     __shared__ int s_apply;
     const int64_t n4 = n >> 2;
-    const int64_t i = (int64_t)blockIdx.x * kUpdThreads + threadIdx.x;
-    // Unconditional loads, the partial first, so that waiting for it leaves
-    // the four element loads in flight (lanes past the end re-read the last
-    // partial / vector and discard it; the host guarantees n >= 4).
+    int64_t c = blockIdx.x;
+    if (RCS_UPD_REGIONS > 1) {  // bijection of [0, nblk): region b % k, position b / k
+        const int64_t nblk = gridDim.x;
+        const int64_t k = RCS_UPD_REGIONS, q = nblk / k, r = nblk % k, x = c % k, j = c / k;
+        c = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+    }
+    const int64_t i = c * kUpdThreads + threadIdx.x;
     const int tp = (int)threadIdx.x < nparts ? (int)threadIdx.x : nparts - 1;
     const double xp = partials[tp];
     const int64_t ic = i < n4 ? i : n4 - 1;
@@ -367,17 +309,11 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
     f32x4 wr = ld_stream(w + ic);
     f32x4 mr = ld_stream(m + ic);
     f32x4 vr = ld_stream(v + ic);
-    const double x = ((int)threadIdx.x < nparts) ? xp : 0.0;
-    const double S = block_sum<kUpdThreads>(x, lds);
+    const ClipScalars cs = final_reduce(((int)threadIdx.x < nparts) ? xp : 0.0, clip, lds);
     if (threadIdx.x == 0) {
-        const double norm = sqrt(S);
-        ClipScalars r;
-        r.norm = norm;
-        r.apply = isfinite(norm) ? 1 : 0;
-        r.scale = (norm > (double)clip) ? (float)((double)clip / norm) : 1.0f;
-        s_scale = r.scale;
-        s_apply = r.apply;
-        if (blockIdx.x == 0) *sc_out = r;
+        s_scale = cs.scale;
+        s_apply = cs.apply;
+        if (blockIdx.x == 0) *sc_out = cs;
     }
     __syncthreads();
     if (!s_apply) return;
@@ -388,6 +324,7 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
         st_stream(m + i, mr);
         st_stream(v + i, vr);
     }
+    // the n % 4 trailing elements
     const int rem = (int)(n & 3);
     if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
         const int64_t k = (n4 << 2) + threadIdx.x;
@@ -608,7 +545,7 @@ void launch_partial(const float *g, int64_t n, float gscale, Workspace *ws, hipS
 int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *ws,
                 hipStream_t stream, hipEvent_t *ev = nullptr) {
     launch_partial(g, n, gscale, ws, stream, ev ? ev[0] : nullptr);
-    hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kFinalThreads), 0, stream, nullptr,
+    hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kParts), 0, stream, nullptr,
                           ev ? ev[1] : nullptr, 0, (const double *)ws->partials, norm_blocks(n),
                           clip, ws->scalars);
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
@@ -618,46 +555,30 @@ bool all_aligned16(const void *a, const void *b, const void *c, const void *d) {
     return aligned16(a) && aligned16(b) && aligned16(c) && aligned16(d);
 }
 
-// Whether the step takes the two-launch form (a2 folded into the update).
-bool fold_final(const float *w, const float *g, const float *m, const float *v, int64_t n) {
-    return RCS_FOLD_FINAL && n >= 4 && norm_blocks(n) <= kFoldMaxParts &&
-           all_aligned16(w, g, m, v);
-}
-
-// a1 then a2 + a3 in one kernel. ev (optional, profiling): ev[0] / ev[1] take
-// the partial kernel's start / end, ev[2] / ev[3] the update's.
-int launch_step_fold(float *w, const float *g, float *m, float *v, int64_t n, float clip,
-                     const StepScalars &h, Workspace *ws, hipStream_t stream,
-                     hipEvent_t *ev = nullptr) {
-    launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
-    const int64_t n4 = n >> 2;
-    int64_t blocks = (n4 + kUpdThreads - 1) / kUpdThreads;
-    if (blocks < 1) blocks = 1;
-    hipExtLaunchKernelGGL(adamw_update_vec_fold, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
-                          stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0,
-                          reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
-                          reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n,
-                          (const double *)ws->partials, norm_blocks(n), clip, ws->scalars, h);
-    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
-}
-
-// ev (optional, profiling): ev[0] and ev[1] take the update kernel's start and end.
-int launch_update(float *w, const float *g, float *m, float *v, int64_t n, const ClipScalars *sc,
-                  const StepScalars &h, hipStream_t stream, hipEvent_t *ev = nullptr) {
-    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-    if (all_aligned16(w, g, m, v)) {
-        const int64_t n4 = n >> 2;
-        int64_t blocks = (n4 + kUpdChunk - 1) / kUpdChunk;
-        if (blocks < 1) blocks = 1;
+// The whole step a1..a3. Vector form (16-byte aligned arrays, n >= 4): the
+// partial kernel, then the update kernel with the final reduction at its head
+// (two launches). Otherwise: partial, final, scalar update (three).
+// ev (optional, profiling): ev[0] / ev[1] take the start of the partial kernel
+// and the end of the last norm kernel, ev[2] / ev[3] the update's start / end.
+int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float clip,
+                const StepScalars &h, Workspace *ws, hipStream_t stream, hipEvent_t *ev) {
+    hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+    if (n >= 4 && all_aligned16(w, g, m, v)) {
+        launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+        const int64_t blocks = ((n >> 2) + kUpdThreads - 1) / kUpdThreads;
         hipExtLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
-                              stream, e0, e1, 0, reinterpret_cast<f32x4 *>(w),
+                              stream, e2, e3, 0, reinterpret_cast<f32x4 *>(w),
                               reinterpret_cast<const f32x4 *>(g), reinterpret_cast<f32x4 *>(m),
-                              reinterpret_cast<f32x4 *>(v), n, sc, h);
+                              reinterpret_cast<f32x4 *>(v), n, (const double *)ws->partials,
+                              norm_blocks(n), clip, ws->scalars, h);
     } else {
+        const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
+        if (rc != RCS_OK) return rc;
         int64_t blocks = (n + kUpdThreads - 1) / kUpdThreads;
         if (blocks > 65536) blocks = 65536;
         hipExtLaunchKernelGGL(adamw_update_scalar, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
-                              stream, e0, e1, 0, w, g, m, v, n, sc, h);
+                              stream, e2, e3, 0, w, g, m, v, n, (const ClipScalars *)ws->scalars,
+                              h);
     }
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
@@ -754,12 +675,7 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
         if (g_prof.on && (g_prof.calls++ % g_prof.every) == 0 && g_prof.next < g_prof.max_records)
             ev = &g_prof.ev[4 * g_prof.next++];
     }
-    if (fold_final(w, g, m, v, n)) {
-        rc = launch_step_fold(w, g, m, v, n, clip, h, ws, stream, ev);
-    } else {
-        if ((rc = launch_norm(g, n, grad_scale, clip, ws, stream, ev)) != RCS_OK) return rc;
-        rc = launch_update(w, g, m, v, n, ws->scalars, h, stream, ev ? ev + 2 : nullptr);
-    }
+    rc = launch_step(w, g, m, v, n, clip, h, ws, stream, ev);
     ws->has_norm = true;
     return rc;
 }

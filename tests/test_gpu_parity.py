@@ -215,11 +215,12 @@ def test_update_parity_stress_subnormals_full_size(dev):
     assert sub.sum() > 0, "stress grads should leave subnormal first moments"
 
 
-# Up to 256 norm partials (n <= 4,194,304, 16-byte aligned arrays) the update
-# kernel reduces the partials itself instead of a separate final kernel; its
-# reduction must give the final kernel's bits. grad_global_norm always runs
-# the final kernel, so the two norms of one gradient must be equal.
-@pytest.mark.parametrize("n", [4, 5, 4099, 262_147, 1_048_576, 4_194_304, 4_194_305, 4_194_308])
+# With 16-byte aligned arrays the update kernel reduces the norm partials
+# itself instead of a separate final kernel; its reduction must give the
+# final kernel's bits. grad_global_norm always runs the final kernel, so the
+# two norms of one gradient must be equal (sizes from one partial to the
+# 256-block cap with several grid-stride passes, ragged tails).
+@pytest.mark.parametrize("n", [4, 5, 4099, 262_147, 2_097_152, 2_097_153, 33_554_435])
 def test_step_norm_same_bits_as_final_kernel(dev, n):
     g = workloads.custom(140, n, 0.01, device=dev)
     g[n // 2] = 3.0  # one large element: the step clips
@@ -238,15 +239,17 @@ def test_step_norm_same_bits_as_final_kernel(dev, n):
         _check_state(w, m, v, ow, om, ov, f"n={n} t={t}")
 
 
-@pytest.mark.parametrize("n", [10_000, 5_000_001])
-def test_nonfinite_norm_skips_update(dev, n):
-    w = workloads.custom(104, n, 0.02, device=dev)
-    m = workloads.custom(105, n, 0.01, device=dev)
-    v = workloads.custom(106, n, 0.01, device=dev).abs_()
+@pytest.mark.parametrize("n,off", [(10_000, 0), (5_000_001, 0), (10_000, 1), (3, 0)])
+def test_nonfinite_norm_skips_update(dev, n, off):
+    """Both update forms skip: the vector kernel (aligned, n >= 4) and the
+    scalar one after the final kernel (unaligned views, n < 4)."""
+    w = workloads.custom(104, n + off, 0.02, device=dev)[off:]
+    m = workloads.custom(105, n + off, 0.01, device=dev)[off:]
+    v = workloads.custom(106, n + off, 0.01, device=dev)[off:].abs_()
     before = [_host(x).copy() for x in (w, m, v)]
     for bad in (float("inf"), float("nan")):
-        g = workloads.custom(107, n, 1.0, device=dev)
-        g[777] = bad
+        g = workloads.custom(107, n + off, 1.0, device=dev)[off:]
+        g[min(777, n - 1)] = bad
         rcs.adamw_clip_step(w, g, m, v, 4, 3e-3, 0.01, 1.0)
         norm = _gpu_norm()
         assert not np.isfinite(norm)

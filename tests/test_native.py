@@ -69,8 +69,8 @@ def test_oracle_under_address_and_ub_sanitizers(tmp_path):
 def test_c_program_trains_and_saves_on_the_gpu(tmp_path, n):
     """A C program drives three updates, the pack, the step-file write and the
     asynchronous writer through the C ABI alone; its norms and its file match
-    the oracle run on the same inputs (n = 100,003 takes the two-launch step,
-    5,000,001 the three-launch one; both have a ragged tail)."""
+    the oracle run on the same inputs (one and several grid-stride passes of
+    the norm kernel; both sizes have a ragged tail)."""
     import numpy as np
 
     import oracle
