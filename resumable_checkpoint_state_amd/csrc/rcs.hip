@@ -83,8 +83,8 @@ namespace {
 
 constexpr int kWave = 64;
 // Norm pass: at most 256 blocks of 512 lanes, 4 loads of 16 B in flight per
-// lane (measured best of 256-1024 lanes x 2-8 loads with 256 blocks, and of
-// the earlier 2048 blocks x 256 lanes with a separate final kernel).
+// lane (measured best of 256-1024 lanes x 2-8 loads with 256 blocks, and
+// faster per step than 2048 blocks x 256 lanes followed by a final kernel).
 constexpr int kNormThreads = 512;
 constexpr int kNormUnroll = 4;
 constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormUnroll;  // vectors per block-iteration
