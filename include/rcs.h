@@ -114,9 +114,10 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
 int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream);
 
 /*
- * The global clip on its own, in place: the norm kernels as in
+ * The global clip on its own, in place: the partial-sum kernel as in
  * adamw_clip_step, then the pages' third clip kernel (the grad_scale of the
- * backprop lesson's pairing-rule table): g[i] = g[i] * s in float32 with
+ * backprop lesson's pairing-rule table), which does the final reduction at
+ * its head like the update kernel: g[i] = g[i] * s in float32 with
  * s = (float)(clip/norm) if norm > clip, else 1. If the norm is not finite,
  * g is left untouched. For callers that need the clipped gradient itself
  * (adamw_clip_step never writes g). g: device float32[n]; clip > 0 (+inf

@@ -368,28 +368,52 @@ __global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restri
 }
 
 // The pages' third clip kernel on its own, for callers that need the clipped
-// gradient itself: g *= s in place (skipped when the norm is not finite).
-// Same float32 product as the update's g * s.
-__global__ __launch_bounds__(256) void grad_scale_vec(f32x4 *__restrict__ g, int64_t n4,
-                                                      const ClipScalars *__restrict__ sc) {
-    if (!sc->apply) return;
-    const float s = sc->scale;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// gradient itself: g *= s in place (skipped when the norm is not finite). Same
+// float32 product as the update's g * s, and the same head as the update
+// kernel: every block first does the final norm reduction (so the in-place
+// clip is two launches), with its element load in flight; block 0 stores the
+// record. Lanes past the end re-read the last vector and discard it (the host
+// guarantees n >= 4); the last block also scales the n % 4 trailing elements.
+__global__ __launch_bounds__(kParts) void grad_scale_vec(f32x4 *__restrict__ g, int64_t n,
+                                                         const double *__restrict__ partials,
+                                                         int nparts, float clip,
+                                                         ClipScalars *__restrict__ sc_out) {
+    __shared__ double lds[kParts / kWave];
+    __shared__ float s_scale;
+    __shared__ int s_apply;
+    const int64_t n4 = n >> 2;
+    const int64_t i = (int64_t)blockIdx.x * kParts + threadIdx.x;
+    const int tp = (int)threadIdx.x < nparts ? (int)threadIdx.x : nparts - 1;
+    const double xp = partials[tp];
+    f32x4 x = __builtin_nontemporal_load(g + (i < n4 ? i : n4 - 1));
+    const ClipScalars cs = final_reduce(((int)threadIdx.x < nparts) ? xp : 0.0, clip, lds);
+    if (threadIdx.x == 0) {
+        s_scale = cs.scale;
+        s_apply = cs.apply;
+        if (blockIdx.x == 0) *sc_out = cs;
+    }
+    __syncthreads();
+    if (!s_apply) return;
+    const float s = s_scale;
     if (i < n4) {
-        f32x4 x = __builtin_nontemporal_load(g + i);
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = x[k] * s;
         __builtin_nontemporal_store(x, g + i);
     }
+    const int rem = (int)(n & 3);
+    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
+        float *gf = reinterpret_cast<float *>(g);
+        const int64_t k = (n4 << 2) + threadIdx.x;
+        gf[k] = gf[k] * s;
+    }
 }
 
-__global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, int64_t begin,
-                                                         int64_t n,
+__global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, int64_t n,
                                                          const ClipScalars *__restrict__ sc) {
     if (!sc->apply) return;
     const float s = sc->scale;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = begin + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
         g[i] = g[i] * s;
 }
 
@@ -701,23 +725,19 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream) {
     if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
     Workspace *ws = nullptr;
     if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
-    if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
-    ws->has_norm = true;
-    int64_t done = 0;
-    if (aligned16(g)) {
-        const int64_t n4 = n >> 2;
-        if (n4 > 0)
-            hipLaunchKernelGGL(grad_scale_vec, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                               stream, reinterpret_cast<f32x4 *>(g), n4,
-                               (const ClipScalars *)ws->scalars);
-        done = n4 << 2;
-    }
-    if (done < n) {
-        int64_t blocks = (n - done + 255) / 256;
+    if (n >= 4 && aligned16(g)) {  // partial, then the scale kernel with the final step at its head
+        launch_partial(g, n, 1.0f, ws, stream);
+        hipLaunchKernelGGL(grad_scale_vec, dim3((unsigned)(((n >> 2) + kParts - 1) / kParts)),
+                           dim3(kParts), 0, stream, reinterpret_cast<f32x4 *>(g), n,
+                           (const double *)ws->partials, norm_blocks(n), clip, ws->scalars);
+    } else {  // unaligned g or n < 4: partial, final, scalar scale
+        if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
+        int64_t blocks = (n + 255) / 256;
         if (blocks > 65536) blocks = 65536;
         hipLaunchKernelGGL(grad_scale_scalar, dim3((unsigned)blocks), dim3(256), 0, stream, g,
-                           done, n, (const ClipScalars *)ws->scalars);
+                           n, (const ClipScalars *)ws->scalars);
     }
+    ws->has_norm = true;
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
