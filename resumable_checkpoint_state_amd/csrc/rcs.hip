@@ -286,7 +286,8 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 // come from L2. The partial is loaded first and every load is unconditional
 // (lanes past the end re-read the last partial / vector and discard it; the
 // host guarantees n >= 4), so waiting for the partial leaves the four element
-// loads in flight during the reduction.
+// loads in flight during the reduction. A discarded re-read of the last
+// vector may overlap its owner lane's store; its value is never used.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
     f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
     f32x4 *__restrict__ v, int64_t n, const double *__restrict__ partials, int nparts, float clip,
