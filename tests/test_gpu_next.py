@@ -31,10 +31,10 @@ def _host(t):
     return t.detach().cpu().numpy()
 
 
-@pytest.mark.parametrize("n_micro", [1, 3, 4])
-def test_accumulated_microbatch_step_parity(dev, n_micro):
+@pytest.mark.parametrize("n_micro,n", [(1, 1_000_003), (3, 1_000_003), (4, 1_000_003),
+                                         (4, 124_356_864)])
+def test_accumulated_microbatch_step_parity(dev, n_micro, n):
     wl = workloads.WORKLOADS["andrea12m"]
-    n = 1_000_003
     w = workloads.init_params(wl, device=dev, n=n)
     m, v = workloads.zeros_like_state(n, device=dev)
     ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)

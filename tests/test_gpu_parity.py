@@ -589,7 +589,7 @@ def test_two_streams_have_separate_workspaces(dev):
 
 @pytest.mark.parametrize("n,offset,sigma", [(1, 0, 5.0), (7, 0, 5.0), (262_147, 0, 0.01),
                                             (1_000_003, 0, 1.0), (100_001, 1, 1.0),
-                                            (12_800_000, 0, 1e-4)])
+                                            (12_800_000, 0, 1e-4), (124_356_866, 0, 1e-4)])
 def test_grad_clip_inplace_parity(dev, n, offset, sigma):
     base = workloads.custom(600, n + offset, sigma, device=dev)
     g = base[offset:]
