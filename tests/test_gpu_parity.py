@@ -587,6 +587,55 @@ def test_two_streams_have_separate_workspaces(dev):
     _check_state(*B, *oB, "stream B")
 
 
+def test_host_threads_each_on_its_own_stream(dev):
+    """Four host threads, each with its own stream and parameters, call the
+    library at once (the ctypes calls release the GIL, so the C library sees
+    concurrent calls, first-use workspace creation included); every result is
+    bit-identical to the same updates run one after another."""
+    import threading
+    sizes = [262_147, 1_000_003, 4099, 3_000_001]
+    steps = 10
+    init = [[workloads.custom(700 + 10 * k + j, n, 0.02 if j == 0 else 0.0, device=dev)
+             for j in range(3)] for k, n in enumerate(sizes)]
+    grads = [[workloads.custom(800 + 10 * k + t, n, 0.05, device=dev) for t in range(steps)]
+             for k, n in enumerate(sizes)]
+    ref = [[x.clone() for x in st] for st in init]
+    for k in range(len(sizes)):
+        for t in range(1, steps + 1):
+            rcs.adamw_clip_step(ref[k][0], grads[k][t - 1], ref[k][1], ref[k][2], t, 3e-3, 0.01, 1.0)
+    states = [[x.clone() for x in st] for st in init]
+    streams = [torch.cuda.Stream() for _ in sizes]
+    norms, errors = [None] * len(sizes), []
+    torch.cuda.synchronize()
+    start = threading.Barrier(len(sizes))
+
+    def work(k):
+        try:
+            torch.cuda.set_device(0)
+            with torch.cuda.stream(streams[k]):
+                start.wait()
+                w, m, v = states[k]
+                for t in range(1, steps + 1):
+                    rcs.adamw_clip_step(w, grads[k][t - 1], m, v, t, 3e-3, 0.01, 1.0)
+                norms[k] = rcs.last_grad_norm()
+            streams[k].synchronize()
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(len(sizes))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for k in range(len(sizes)):
+        for a, b in zip(states[k], ref[k]):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), sizes[k]
+        seq = float(rcs.grad_global_norm(grads[k][-1]).cpu())
+        assert float(norms[k].cpu()) == seq
+
+
 @pytest.mark.parametrize("n,offset,sigma", [(1, 0, 5.0), (7, 0, 5.0), (262_147, 0, 0.01),
                                             (1_000_003, 0, 1.0), (100_001, 1, 1.0),
                                             (12_800_000, 0, 1e-4), (124_356_866, 0, 1e-4)])
