@@ -84,11 +84,11 @@ int rcs_init(int device, hipStream_t stream);
  * If the norm is not finite the update is skipped on the device (w, m, v are
  * left untouched); read the norm with last_grad_norm.
  * The reduction order depends only on n, so results are deterministic.
- * With 16-byte aligned arrays and n >= 4 the step is two launches (the
- * partial sums, then the update kernel, which does the final reduction in
- * grad_norm_final's order: the same norm bits as grad_global_norm); other
- * arrays take partial, final and a scalar update kernel with the same
- * arithmetic.
+ * With 16-byte aligned arrays and n >= 4 the update kernel streams 16-byte
+ * vectors; up to n = 8,388,608 it also does the final reduction itself, in
+ * grad_norm_final's order (two launches instead of three; the same norm bits
+ * as grad_global_norm). Other arrays take partial, final and a scalar update
+ * kernel with the same arithmetic.
  */
 int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                     float lr, float wd, float clip, hipStream_t stream);
@@ -114,10 +114,10 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
 int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream);
 
 /*
- * The global clip on its own, in place: the partial-sum kernel as in
+ * The global clip on its own, in place: the norm kernels as in
  * adamw_clip_step, then the pages' third clip kernel (the grad_scale of the
- * backprop lesson's pairing-rule table), which does the final reduction at
- * its head like the update kernel: g[i] = g[i] * s in float32 with
+ * backprop lesson's pairing-rule table; up to n = 8,388,608 it does the final
+ * reduction itself, as the update kernel does): g[i] = g[i] * s in float32 with
  * s = (float)(clip/norm) if norm > clip, else 1. If the norm is not finite,
  * g is left untouched. For callers that need the clipped gradient itself
  * (adamw_clip_step never writes g). g: device float32[n]; clip > 0 (+inf

@@ -22,20 +22,22 @@
 //     partial per block. The last 320 MB of g are read with cache-allocating
 //     loads so that the part of g still in the 256 MB last-level cache serves
 //     the update's second read; the rest streams.
-//   * adamw_update_vec: each block first sums the <= 256 partials in a fixed
-//     tree (grad_norm_final's step, folded in: one launch and one kernel
-//     boundary fewer per step), takes the float64 square root and the clip
-//     factor, then streams one 16-byte vector of w, g, m, v per lane (16 B read
-//     + 12 B written per element) with streaming loads and stores. Each XCD
-//     streams its own contiguous eighth of the vectors (block b works in
-//     region b % 8, blocks being dispatched round-robin over the 8 XCDs),
-//     which evens out DRAM contention between the seven streams. No float
-//     atomics anywhere, so the result depends only on n and the data. (A
-//     single kernel whose last block does the final step needs a device-scope
-//     release per block, which on this chip costs an L2 write-back per block
-//     and measured slower.)
-//   * grad_norm_final: the same final step as a kernel of its own, for the
-//     norm alone, the in-place clip and the scalar (unaligned) update.
+//   * grad_norm_final: one wave sums the <= 256 partials in a fixed tree
+//     (4 per lane, then the wave butterfly), takes the float64 square root and
+//     writes {norm, clip factor, apply flag}. No float atomics anywhere, so
+//     the result depends only on n and the data. (A single kernel whose last
+//     block does this step needs a device-scope release per block, which on
+//     this chip costs an L2 write-back per block and measured slower.)
+//   * adamw_update_vec: one wave per block, one 16-byte vector of w, g, m, v
+//     per lane (16 B read + 12 B written per element) with streaming loads
+//     and stores; the clip factor comes from device memory, so the host never
+//     waits between kernels. Each XCD streams its own contiguous eighth of the
+//     vectors (block b works in region b % 8, blocks being dispatched
+//     round-robin over the 8 XCDs), which evens out DRAM contention between
+//     the seven streams.
+//   * adamw_update_vec_fold: for n up to 8,388,608, where the step is bound
+//     by launch cost, every wave does grad_norm_final's reduction itself (the
+//     same bits) and the step is two launches instead of three.
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -75,6 +77,12 @@
 // allocating) loads so that the update, which reads g again right after,
 // finds them in the last-level cache; the rest is read with streaming loads.
 // A negative value reads all of g with ordinary loads.
+// Largest n whose step folds the final norm reduction into the update kernel
+// (measured: folding saves 1.7-2.4 us per step up to 8,388,608 elements and
+// costs 4.8 us at 16,777,216 and 23 us at 124,356,864).
+#ifndef RCS_FOLD_MAX_N
+#define RCS_FOLD_MAX_N 8388608
+#endif
 #ifndef RCS_NORM_CACHED_TAIL_BYTES
 #define RCS_NORM_CACHED_TAIL_BYTES (320LL << 20)
 #endif
@@ -89,11 +97,20 @@ constexpr int kNormThreads = 512;
 constexpr int kNormUnroll = 4;
 constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormUnroll;  // vectors per block-iteration
 constexpr int kNormMaxBlocks = 256;
-// The final reduction (grad_norm_final, and the head of the update kernel)
-// gives lane i partial i; both use blocks of this many lanes.
-constexpr int kParts = 256;
-constexpr int kUpdThreads = kParts;  // update: one 16-byte vector of each array per lane
-static_assert(kNormMaxBlocks <= kParts, "one partial per lane in the final reduction");
+// At most this many partials reach the final reduction.
+constexpr int kParts = kNormMaxBlocks;
+// Lanes per block of the update and in-place scale kernels, one 16-byte
+// vector of each array per lane; the final reduction (in those kernels and in
+// grad_norm_final) runs on blocks of the same size, lane i summing partials
+// i, i + L, i + 2L, ... in that order, so all three give the same bits.
+// One wave per block measured fastest: the update takes 529.7 us at the
+// ANDREA-120M size against 546.1 us with 256 lanes (same process).
+#ifndef RCS_UPD_THREADS
+#define RCS_UPD_THREADS 64
+#endif
+constexpr int kUpdThreads = RCS_UPD_THREADS;
+static_assert(kUpdThreads == 64 || kUpdThreads == 128 || kUpdThreads == 256, "lanes per block");
+constexpr int kPartsPerLane = kParts / kUpdThreads;
 
 // Native 16-byte vector (the nontemporal builtins need a clang vector type).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -208,11 +225,37 @@ __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *_
     if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
-// a2 as a device function: lane i of a kParts-lane block holds partial i (0
-// beyond nparts); the fixed wave/LDS tree sums them, then thread 0 takes the
-// float64 square root and the clip factor. The result is valid in thread 0.
-__device__ __forceinline__ ClipScalars final_reduce(double x, float clip, double *lds) {
-    const double S = block_sum<kParts>(x, lds);
+// a2, first half: lane i of a kUpdThreads-lane block loads partials i, i + L,
+// i + 2L, ... (L = kUpdThreads). Every load is issued (lanes past nparts
+// re-read the last partial; final_reduce drops them), so that a caller can
+// issue its own loads behind these and still wait for these alone.
+__device__ __forceinline__ void load_partials(const double *__restrict__ partials, int nparts,
+                                              double (&x)[kPartsPerLane]) {
+#pragma unroll
+    for (int k = 0; k < kPartsPerLane; ++k) {
+        const int j = (int)threadIdx.x + k * kUpdThreads;
+        x[k] = partials[j < nparts ? j : nparts - 1];
+    }
+}
+
+// a2, second half: each lane sums its partials in index order (0 beyond
+// nparts), the block sums the lanes in the fixed wave/LDS tree, then the
+// float64 square root and the clip factor. The result is valid in every lane.
+__device__ __forceinline__ ClipScalars final_reduce(const double (&x)[kPartsPerLane], int nparts,
+                                                    float clip, double *lds) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPartsPerLane; ++k)
+        acc += ((int)threadIdx.x + k * kUpdThreads < nparts) ? x[k] : 0.0;
+    double S;
+    if constexpr (kUpdThreads == kWave) {
+        S = wave_sum(acc);  // the same bits in every lane
+    } else {
+        const double b = block_sum<kUpdThreads>(acc, lds);
+        if (threadIdx.x == 0) lds[0] = b;  // block_sum's reads of lds are done by now
+        __syncthreads();
+        S = lds[0];
+    }
     ClipScalars r;
     r.norm = sqrt(S);
     r.apply = isfinite(r.norm) ? 1 : 0;
@@ -220,14 +263,15 @@ __device__ __forceinline__ ClipScalars final_reduce(double x, float clip, double
     return r;
 }
 
-// a2 as its own kernel (the norm alone, the in-place clip, and the scalar
-// update path): one kParts-lane block writes {norm, clip factor, apply flag}.
-__global__ __launch_bounds__(kParts) void grad_norm_final(const double *__restrict__ partials,
-                                                          int nparts, float clip,
-                                                          ClipScalars *__restrict__ out) {
-    __shared__ double lds[kParts / kWave];
-    const double x = ((int)threadIdx.x < nparts) ? partials[threadIdx.x] : 0.0;
-    const ClipScalars r = final_reduce(x, clip, lds);
+// a2 as its own kernel (the norm alone, and the unaligned / n < 4 paths):
+// one kUpdThreads-lane block writes {norm, clip factor, apply flag}.
+__global__ __launch_bounds__(kUpdThreads) void grad_norm_final(const double *__restrict__ partials,
+                                                               int nparts, float clip,
+                                                               ClipScalars *__restrict__ out) {
+    __shared__ double lds[kUpdThreads / kWave];
+    double x[kPartsPerLane];
+    load_partials(partials, nparts, x);
+    const ClipScalars r = final_reduce(x, nparts, clip, lds);
     if (threadIdx.x == 0) *out = r;
 }
 
@@ -278,23 +322,25 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 #endif
 }
 
-// a2 + a3: every block first reduces the norm partials (the final kernel's
-// tree, so the same bits), then applies the clip factor and AdamW to one
-// 16-byte vector of w, g, m, v per lane, with streaming loads and stores;
-// block 0 also stores the record last_grad_norm reads. Folding a2 in saves a
-// launch and a kernel boundary per step; the 2 KB of partials each block reads
-// come from L2. The partial is loaded first and every load is unconditional
-// (lanes past the end re-read the last partial / vector and discard it; the
-// host guarantees n >= 4), so waiting for the partial leaves the four element
-// loads in flight during the reduction. A discarded re-read of the last
-// vector may overlap its owner lane's store; its value is never used.
-__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
-    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, const double *__restrict__ partials, int nparts, float clip,
-    ClipScalars *__restrict__ sc_out, StepScalars h) {
-    __shared__ double lds[kParts / kWave];
-    __shared__ float s_scale;
-    __shared__ int s_apply;
+// a3: clip factor and AdamW on one 16-byte vector of w, g, m, v per lane, with
+// streaming loads and stores; block b works in region b % 8 (one contiguous
+// region per XCD). Every load is unconditional (lanes past the end re-read the
+// last vector and discard it; the host guarantees n >= 4; a discarded re-read
+// may overlap the owner lane's store, and its value is never used).
+// FOLD = false: the clip record comes from grad_norm_final, launched before.
+// FOLD = true: every block first does grad_norm_final's reduction itself (same
+// order, same bits; block 0 stores the record), saving a launch, which pays
+// only while launches are the cost; the partial loads go out first so that
+// waiting for them leaves the element loads in flight. At large n the
+// per-wave float64 square root and division cost more than the launch (one
+// wave per block: 529.7 against 552.2 us for the update at the ANDREA-120M
+// size, measured in one process).
+template <bool FOLD>
+__device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *__restrict__ g,
+                                            f32x4 *__restrict__ m, f32x4 *__restrict__ v,
+                                            int64_t n, const double *__restrict__ partials,
+                                            int nparts, float clip, ClipScalars *__restrict__ sc,
+                                            const StepScalars &h, double *lds) {
     const int64_t n4 = n >> 2;
     int64_t c = blockIdx.x;
     if (RCS_UPD_REGIONS > 1) {  // bijection of [0, nblk): region b % k, position b / k
@@ -303,22 +349,22 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
         c = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
     }
     const int64_t i = c * kUpdThreads + threadIdx.x;
-    const int tp = (int)threadIdx.x < nparts ? (int)threadIdx.x : nparts - 1;
-    const double xp = partials[tp];
+    double xp[kPartsPerLane];
+    if constexpr (FOLD) load_partials(partials, nparts, xp);
     const int64_t ic = i < n4 ? i : n4 - 1;
     f32x4 gr = ld_stream(g + ic);
     f32x4 wr = ld_stream(w + ic);
     f32x4 mr = ld_stream(m + ic);
     f32x4 vr = ld_stream(v + ic);
-    const ClipScalars cs = final_reduce(((int)threadIdx.x < nparts) ? xp : 0.0, clip, lds);
-    if (threadIdx.x == 0) {
-        s_scale = cs.scale;
-        s_apply = cs.apply;
-        if (blockIdx.x == 0) *sc_out = cs;
+    ClipScalars cs;
+    if constexpr (FOLD) {
+        cs = final_reduce(xp, nparts, clip, lds);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *sc = cs;
+    } else {
+        cs = *sc;
     }
-    __syncthreads();
-    if (!s_apply) return;
-    const float s = s_scale;
+    if (!cs.apply) return;
+    const float s = cs.scale;
     if (i < n4) {
         adamw_vec4(wr, gr, mr, vr, s, h);
         st_stream(w + i, wr);
@@ -339,6 +385,23 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
         mf[k] = mm;
         vf[k] = vv;
     }
+}
+
+// a3 after grad_norm_final.
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
+    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ v, int64_t n, const ClipScalars *__restrict__ sc, StepScalars h) {
+    update_body<false>(w, g, m, v, n, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), h,
+                       nullptr);
+}
+
+// a2 + a3 in one kernel (small n).
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
+    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ v, int64_t n, const double *__restrict__ partials, int nparts, float clip,
+    ClipScalars *__restrict__ sc_out, StepScalars h) {
+    __shared__ double lds[kUpdThreads / kWave];
+    update_body<true>(w, g, m, v, n, partials, nparts, clip, sc_out, h, lds);
 }
 
 // a3 for arrays that are not all 16-byte aligned: same arithmetic per element.
@@ -370,32 +433,28 @@ __global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restri
 
 // The pages' third clip kernel on its own, for callers that need the clipped
 // gradient itself: g *= s in place (skipped when the norm is not finite). Same
-// float32 product as the update's g * s, and the same head as the update
-// kernel: every block first does the final norm reduction (so the in-place
-// clip is two launches), with its element load in flight; block 0 stores the
-// record. Lanes past the end re-read the last vector and discard it (the host
-// guarantees n >= 4); the last block also scales the n % 4 trailing elements.
-__global__ __launch_bounds__(kParts) void grad_scale_vec(f32x4 *__restrict__ g, int64_t n,
-                                                         const double *__restrict__ partials,
-                                                         int nparts, float clip,
-                                                         ClipScalars *__restrict__ sc_out) {
-    __shared__ double lds[kParts / kWave];
-    __shared__ float s_scale;
-    __shared__ int s_apply;
+// float32 product as the update's g * s. Lanes past the end re-read the last
+// vector and discard it (the host guarantees n >= 4); the last block also
+// scales the n % 4 trailing elements. FOLD as in update_body: the record from
+// grad_norm_final, or the final reduction at the head of every block.
+template <bool FOLD>
+__device__ __forceinline__ void scale_body(f32x4 *__restrict__ g, int64_t n,
+                                           const double *__restrict__ partials, int nparts,
+                                           float clip, ClipScalars *__restrict__ sc, double *lds) {
     const int64_t n4 = n >> 2;
-    const int64_t i = (int64_t)blockIdx.x * kParts + threadIdx.x;
-    const int tp = (int)threadIdx.x < nparts ? (int)threadIdx.x : nparts - 1;
-    const double xp = partials[tp];
+    const int64_t i = (int64_t)blockIdx.x * kUpdThreads + threadIdx.x;
+    double xp[kPartsPerLane];
+    if constexpr (FOLD) load_partials(partials, nparts, xp);
     f32x4 x = __builtin_nontemporal_load(g + (i < n4 ? i : n4 - 1));
-    const ClipScalars cs = final_reduce(((int)threadIdx.x < nparts) ? xp : 0.0, clip, lds);
-    if (threadIdx.x == 0) {
-        s_scale = cs.scale;
-        s_apply = cs.apply;
-        if (blockIdx.x == 0) *sc_out = cs;
+    ClipScalars cs;
+    if constexpr (FOLD) {
+        cs = final_reduce(xp, nparts, clip, lds);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *sc = cs;
+    } else {
+        cs = *sc;
     }
-    __syncthreads();
-    if (!s_apply) return;
-    const float s = s_scale;
+    if (!cs.apply) return;
+    const float s = cs.scale;
     if (i < n4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = x[k] * s;
@@ -407,6 +466,18 @@ __global__ __launch_bounds__(kParts) void grad_scale_vec(f32x4 *__restrict__ g, 
         const int64_t k = (n4 << 2) + threadIdx.x;
         gf[k] = gf[k] * s;
     }
+}
+
+__global__ __launch_bounds__(kUpdThreads) void grad_scale_vec(f32x4 *__restrict__ g, int64_t n,
+                                                              const ClipScalars *__restrict__ sc) {
+    scale_body<false>(g, n, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), nullptr);
+}
+
+__global__ __launch_bounds__(kUpdThreads) void grad_scale_vec_fold(
+    f32x4 *__restrict__ g, int64_t n, const double *__restrict__ partials, int nparts, float clip,
+    ClipScalars *__restrict__ sc_out) {
+    __shared__ double lds[kUpdThreads / kWave];
+    scale_body<true>(g, n, partials, nparts, clip, sc_out, lds);
 }
 
 __global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, int64_t n,
@@ -570,7 +641,7 @@ void launch_partial(const float *g, int64_t n, float gscale, Workspace *ws, hipS
 int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *ws,
                 hipStream_t stream, hipEvent_t *ev = nullptr) {
     launch_partial(g, n, gscale, ws, stream, ev ? ev[0] : nullptr);
-    hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kParts), 0, stream, nullptr,
+    hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kUpdThreads), 0, stream, nullptr,
                           ev ? ev[1] : nullptr, 0, (const double *)ws->partials, norm_blocks(n),
                           clip, ws->scalars);
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
@@ -580,22 +651,38 @@ bool all_aligned16(const void *a, const void *b, const void *c, const void *d) {
     return aligned16(a) && aligned16(b) && aligned16(c) && aligned16(d);
 }
 
+// Whether the vector kernels do the final reduction themselves (two launches)
+// rather than after grad_norm_final (three): only while the launch it saves
+// costs more than the reduction at the head of every wave.
+bool fold_final(int64_t n) { return n <= (int64_t)RCS_FOLD_MAX_N; }
+
 // The whole step a1..a3. Vector form (16-byte aligned arrays, n >= 4): the
-// partial kernel, then the update kernel with the final reduction at its head
-// (two launches). Otherwise: partial, final, scalar update (three).
+// partial kernel, [grad_norm_final,] the update kernel. Otherwise: partial,
+// final, scalar update.
 // ev (optional, profiling): ev[0] / ev[1] take the start of the partial kernel
 // and the end of the last norm kernel, ev[2] / ev[3] the update's start / end.
 int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float clip,
                 const StepScalars &h, Workspace *ws, hipStream_t stream, hipEvent_t *ev) {
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
     if (n >= 4 && all_aligned16(w, g, m, v)) {
-        launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
         const int64_t blocks = ((n >> 2) + kUpdThreads - 1) / kUpdThreads;
-        hipExtLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads), 0,
-                              stream, e2, e3, 0, reinterpret_cast<f32x4 *>(w),
-                              reinterpret_cast<const f32x4 *>(g), reinterpret_cast<f32x4 *>(m),
-                              reinterpret_cast<f32x4 *>(v), n, (const double *)ws->partials,
-                              norm_blocks(n), clip, ws->scalars, h);
+        f32x4 *w4 = reinterpret_cast<f32x4 *>(w), *m4 = reinterpret_cast<f32x4 *>(m);
+        f32x4 *v4 = reinterpret_cast<f32x4 *>(v);
+        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(g);
+        if (fold_final(n)) {
+            launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr,
+                           ev ? ev[1] : nullptr);
+            hipExtLaunchKernelGGL(adamw_update_vec_fold, dim3((unsigned)blocks),
+                                  dim3(kUpdThreads), 0, stream, e2, e3, 0, w4, g4, m4, v4, n,
+                                  (const double *)ws->partials, norm_blocks(n), clip, ws->scalars,
+                                  h);
+        } else {
+            const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
+            if (rc != RCS_OK) return rc;
+            hipExtLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads),
+                                  0, stream, e2, e3, 0, w4, g4, m4, v4, n,
+                                  (const ClipScalars *)ws->scalars, h);
+        }
     } else {
         const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
         if (rc != RCS_OK) return rc;
@@ -726,11 +813,18 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream) {
     if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
     Workspace *ws = nullptr;
     if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
-    if (n >= 4 && aligned16(g)) {  // partial, then the scale kernel with the final step at its head
-        launch_partial(g, n, 1.0f, ws, stream);
-        hipLaunchKernelGGL(grad_scale_vec, dim3((unsigned)(((n >> 2) + kParts - 1) / kParts)),
-                           dim3(kParts), 0, stream, reinterpret_cast<f32x4 *>(g), n,
-                           (const double *)ws->partials, norm_blocks(n), clip, ws->scalars);
+    if (n >= 4 && aligned16(g)) {  // partial, [final,] the vector scale kernel
+        const dim3 grid((unsigned)(((n >> 2) + kUpdThreads - 1) / kUpdThreads));
+        if (fold_final(n)) {
+            launch_partial(g, n, 1.0f, ws, stream);
+            hipLaunchKernelGGL(grad_scale_vec_fold, grid, dim3(kUpdThreads), 0, stream,
+                               reinterpret_cast<f32x4 *>(g), n, (const double *)ws->partials,
+                               norm_blocks(n), clip, ws->scalars);
+        } else {
+            if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
+            hipLaunchKernelGGL(grad_scale_vec, grid, dim3(kUpdThreads), 0, stream,
+                               reinterpret_cast<f32x4 *>(g), n, (const ClipScalars *)ws->scalars);
+        }
     } else {  // unaligned g or n < 4: partial, final, scalar scale
         if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
         int64_t blocks = (n + 255) / 256;

@@ -215,12 +215,13 @@ def test_update_parity_stress_subnormals_full_size(dev):
     assert sub.sum() > 0, "stress grads should leave subnormal first moments"
 
 
-# With 16-byte aligned arrays the update kernel reduces the norm partials
-# itself instead of a separate final kernel; its reduction must give the
-# final kernel's bits. grad_global_norm always runs the final kernel, so the
-# two norms of one gradient must be equal (sizes from one partial to the
-# 256-block cap with several grid-stride passes, ragged tails).
-@pytest.mark.parametrize("n", [4, 5, 4099, 262_147, 2_097_152, 2_097_153, 33_554_435])
+# With 16-byte aligned arrays and n up to 8,388,608 the update kernel reduces
+# the norm partials itself instead of a separate final kernel; its reduction
+# must give the final kernel's bits. grad_global_norm always runs the final
+# kernel, so the two norms of one gradient must be equal (sizes from one
+# partial to the 256-block cap, both sides of the fold limit, ragged tails).
+@pytest.mark.parametrize("n", [4, 5, 4099, 262_147, 2_097_152, 2_097_153, 8_388_608, 8_388_611,
+                               33_554_435])
 def test_step_norm_same_bits_as_final_kernel(dev, n):
     g = workloads.custom(140, n, 0.01, device=dev)
     g[n // 2] = 3.0  # one large element: the step clips
@@ -638,7 +639,8 @@ def test_host_threads_each_on_its_own_stream(dev):
 
 @pytest.mark.parametrize("n,offset,sigma", [(1, 0, 5.0), (7, 0, 5.0), (262_147, 0, 0.01),
                                             (1_000_003, 0, 1.0), (100_001, 1, 1.0),
-                                            (12_800_000, 0, 1e-4), (124_356_866, 0, 1e-4)])
+                                            (8_388_611, 0, 1e-4), (12_800_000, 0, 1e-4),
+                                            (124_356_866, 0, 1e-4)])
 def test_grad_clip_inplace_parity(dev, n, offset, sigma):
     base = workloads.custom(600, n + offset, sigma, device=dev)
     g = base[offset:]
