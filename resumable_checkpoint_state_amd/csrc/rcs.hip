@@ -65,8 +65,10 @@
 // Contiguous regions of the vectors the update streams at once: block b
 // works in region b % k. Blocks are dispatched round-robin over the chip's 8
 // XCDs, so with k = 8 each XCD streams its own contiguous eighth of w, g, m, v.
-// Measured across buffer placements this keeps the update at 543-558 us at the
-// ANDREA-120M size where plain address order (k = 1) ranges 548-595 us.
+// With one-wave blocks, over 14 buffer placements on one box the step took
+// 605.0-619.3 us (mean 611.0) with k = 8 against 612.9-631.1 (617.5) with
+// k = 4 (6 placements on another box: means 609.9 and 608.0; k = 2, 1, 16
+// and 32 were slower).
 #ifndef RCS_UPD_REGIONS
 #define RCS_UPD_REGIONS 8
 #endif
@@ -323,7 +325,7 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 }
 
 // a3: clip factor and AdamW on one 16-byte vector of w, g, m, v per lane, with
-// streaming loads and stores; block b works in region b % 8 (one contiguous
+// streaming loads and stores; block b works in contiguous region b % 8 (one
 // region per XCD). Every load is unconditional (lanes past the end re-read the
 // last vector and discard it; the host guarantees n >= 4; a discarded re-read
 // may overlap the owner lane's store, and its value is never used).
