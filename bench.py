@@ -273,6 +273,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the update path runs per GPU and no "
