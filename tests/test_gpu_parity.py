@@ -702,3 +702,23 @@ def test_abi_rejects_host_and_short_device_buffers(dev):
     assert rc in (rcs.ESIZE, rcs.OK)  # ESIZE unless the allocator packed it inside a larger block
     assert L.adamw_clip_step(p[0], p[0], p[2], p[3], n, 1, 1e-3, 0.0, 1.0, stream) == rcs.EINVAL
     torch.cuda.synchronize()
+
+
+def test_init_and_last_norm_rejections(dev):
+    """rcs_init refuses a device that does not exist; last_grad_norm on a
+    stream that has run nothing yet is refused rather than returning stale
+    or uninitialised memory."""
+    with pytest.raises(rcs.RcsError) as e:
+        rcs.init(device=torch.cuda.device_count() + 7)
+    assert e.value.status == rcs.EINVAL
+    fresh = torch.cuda.Stream()
+    rcs.init(stream=fresh)  # the workspace exists, but no norm has been computed on it
+    with pytest.raises(rcs.RcsError) as e:
+        rcs.last_grad_norm(stream=fresh)
+    assert e.value.status == rcs.EINVAL
+    g = workloads.custom(900, 1000, 1.0, device=dev)
+    torch.cuda.synchronize()  # g was written on the default stream
+    with torch.cuda.stream(fresh):
+        rcs.grad_global_norm(g)
+        got = float(rcs.last_grad_norm().cpu())
+    assert abs(got - oracle.grad_norm(_host(g))) <= NORM_RTOL * got
