@@ -2,8 +2,9 @@
 include/rcs.h compiles as C and a C program links and calls librcs.so (host
 rejections here; a whole C training loop with pack, file write and the
 asynchronous writer on the GPU, checked against the oracle); the host
-file-IO code runs under AddressSanitizer and UndefinedBehaviorSanitizer
-(host code only: no device code is built with a sanitizer)."""
+file-IO code runs under AddressSanitizer and UndefinedBehaviorSanitizer, the
+asynchronous writer under ThreadSanitizer (host code only: no device code is
+built with a sanitizer)."""
 import os
 import shutil
 import subprocess
@@ -50,6 +51,23 @@ def test_file_io_under_address_and_ub_sanitizers(tmp_path):
     d.mkdir()
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0")
     assert "ckpt_io driver ok" in _run([str(exe), str(d)], env=env)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not installed")
+def test_async_writer_under_thread_sanitizer(tmp_path):
+    """The asynchronous writer's worker thread, lock and condition variable
+    under ThreadSanitizer, with concurrent submit and wait calls; the device
+    side is a host stand-in (tests/native/writer_tsan_driver.cpp), the file
+    side the real ckpt_io.cpp."""
+    exe = tmp_path / "writer_tsan_driver"
+    csrc = os.path.join(ROOT, "resumable_checkpoint_state_amd", "csrc")
+    _run(["g++", "-std=c++17", "-g", "-O1", "-fsanitize=thread", *HIP_DEFS, f"-I{csrc}",
+          os.path.join(csrc, "ckpt_writer.cpp"), os.path.join(csrc, "ckpt_io.cpp"),
+          os.path.join(NATIVE, "writer_tsan_driver.cpp"), "-o", str(exe), "-lpthread"])
+    d = tmp_path / "files"
+    d.mkdir()
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1")
+    assert "writer tsan driver ok" in _run([str(exe), str(d)], env=env)
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
