@@ -797,7 +797,7 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
             ev = &g_prof.ev[4 * g_prof.next++];
     }
     rc = launch_step(w, g, m, v, n, clip, h, ws, stream, ev);
-    ws->has_norm = true;
+    if (rc == RCS_OK) ws->has_norm = true;
     return rc;
 }
 
@@ -841,8 +841,9 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream) {
         hipLaunchKernelGGL(grad_scale_scalar, dim3((unsigned)blocks), dim3(256), 0, stream, g,
                            n, (const ClipScalars *)ws->scalars);
     }
+    if (hipGetLastError() != hipSuccess) return RCS_EHIP;
     ws->has_norm = true;
-    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
+    return RCS_OK;
 }
 
 int last_grad_norm(hipStream_t stream, double *norm_out) {
