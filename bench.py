@@ -60,7 +60,8 @@ def measured_traffic():
     or None when there is none or the kernel source changed since."""
     if not os.path.exists(PMC_SUMMARY):
         return None
-    text = open(PMC_SUMMARY).read()
+    with open(PMC_SUMMARY) as f:
+        text = f.read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not h or not t or h.group(1) != kernel_source_hash():
@@ -82,10 +83,11 @@ def cpu_baseline(wl, budget_s: float):
     g = workloads.grads(wl, 1).numpy()
     cpu_model = "unknown"
     try:
-        for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                cpu_model = ln.split(":", 1)[1].strip()
-                break
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
     except OSError:
         pass
     allowed = sorted(os.sched_getaffinity(0))

@@ -121,7 +121,8 @@ def verify_sharded(directory, expected_world_size: int, n: int):
     path = os.path.join(directory, MANIFEST)
     if not os.path.exists(path):
         raise ShardError(f"no manifest in {directory} (checkpoint incomplete)")
-    man = ShardManifest.from_json(open(path).read())
+    with open(path) as f:
+        man = ShardManifest.from_json(f.read())
     if man.schema_version != SCHEMA_VERSION:
         raise ShardError(f"schema_version {man.schema_version}, expected {SCHEMA_VERSION}")
     if man.world_size != expected_world_size:
@@ -147,7 +148,8 @@ def verify_sharded(directory, expected_world_size: int, n: int):
         fpath = os.path.join(directory, s.path)
         if not os.path.exists(fpath):
             raise ShardError(f"rank {s.rank}: missing shard file {s.path}")
-        raw = open(fpath, "rb").read()
+        with open(fpath, "rb") as f:
+            raw = f.read()
         if hashlib.sha256(raw).hexdigest() != s.sha256:
             raise ShardError(f"rank {s.rank}: sha256 mismatch (partial or corrupted write)")
         if len(raw) != ckpt_bytes(s.param_shard_numel):
