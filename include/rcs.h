@@ -83,9 +83,13 @@ int rcs_init(int device, hipStream_t stream);
  * decay = (float)(1 - (double)lr*(double)wd) are computed on the host.
  * If the norm is not finite the update is skipped on the device (w, m, v are
  * left untouched); read the norm with last_grad_norm.
- * The reduction order depends only on n, so results are deterministic.
- * With 16-byte aligned arrays and n >= 4 the update kernel streams 16-byte
- * vectors; up to n = 8,388,608 it also does the final reduction itself, in
+ * The reduction order depends only on n and on g's address modulo 256
+ * bytes, so results are deterministic for a given buffer.
+ * When w, g, m and v lie equally far (0, 4, 8 or 12 bytes) from a 16-byte
+ * boundary, the update kernel streams 16-byte vectors from w's next 256-byte
+ * boundary on and takes the 0-63 elements before it separately (with fewer
+ * than 4 elements after that boundary: from the next 16-byte one); up to
+ * n = 8,388,608 it also does the final reduction itself, in
  * grad_norm_final's order (two launches instead of three; the same norm bits
  * as grad_global_norm). Other arrays take partial, final and a scalar update
  * kernel with the same arithmetic.

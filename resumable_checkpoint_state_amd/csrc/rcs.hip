@@ -178,10 +178,12 @@ __device__ __forceinline__ double sq(float x, float gscale) {
     return d * d;
 }
 
-// a1: per-block float64 partial sums of squares. The first nt_limit4 vectors
-// are read with streaming loads, the rest with cache-allocating loads.
+// a1: per-block float64 partial sums of squares. head >= 0 (at most 63):
+// g + head is 16-byte aligned; its vectors are read with 16-byte loads (the first
+// nt_limit4 streaming, the rest cache-allocating), block 0 adds the head
+// elements before it and the n % 4 after it. head < 0: scalar loads only.
 __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *__restrict__ g,
-                                                                  int64_t n, int vec_ok,
+                                                                  int64_t n, int head,
                                                                   int64_t nt_limit4, float gscale,
                                                                   double *__restrict__ partials) {
     __shared__ double lds[kNormThreads / kWave];
@@ -189,7 +191,10 @@ __global__ __launch_bounds__(kNormThreads) void grad_norm_partial(const float *_
 #pragma unroll
     for (int j = 0; j < kNormUnroll; ++j) acc[j] = 0.0;
     const int64_t nblk = gridDim.x;
-    if (vec_ok) {
+    if (head >= 0) {
+        if (blockIdx.x == 0 && (int)threadIdx.x < head) acc[1] += sq(g[threadIdx.x], gscale);
+        g += head;
+        n -= head;
         const f32x4 *__restrict__ g4 = reinterpret_cast<const f32x4 *>(g);
         const int64_t n4 = n >> 2;
         for (int64_t base = (int64_t)blockIdx.x * kNormChunk; base < n4; base += nblk * kNormChunk) {
@@ -340,8 +345,9 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 template <bool FOLD>
 __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *__restrict__ g,
                                             f32x4 *__restrict__ m, f32x4 *__restrict__ v,
-                                            int64_t n, const double *__restrict__ partials,
-                                            int nparts, float clip, ClipScalars *__restrict__ sc,
+                                            int64_t n, int head,
+                                            const double *__restrict__ partials, int nparts,
+                                            float clip, ClipScalars *__restrict__ sc,
                                             const StepScalars &h, double *lds) {
     const int64_t n4 = n >> 2;
     int64_t c = blockIdx.x;
@@ -373,14 +379,22 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *
         st_stream(m + i, mr);
         st_stream(v + i, vr);
     }
-    // the n % 4 trailing elements
-    const int rem = (int)(n & 3);
-    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
+    // block 0: the head elements before the body (indices -head .. -1);
+    // the last block: the n % 4 after the last vector
+    float *wf = reinterpret_cast<float *>(w);
+    float *mf = reinterpret_cast<float *>(m);
+    float *vf = reinterpret_cast<float *>(v);
+    const float *gf = reinterpret_cast<const float *>(g);
+    if (blockIdx.x == 0 && (int)threadIdx.x < head) {
+        const int64_t k = (int64_t)threadIdx.x - head;
+        float ww = wf[k], mm = mf[k], vv = vf[k];
+        adamw_elem(ww, gf[k], mm, vv, s, h);
+        wf[k] = ww;
+        mf[k] = mm;
+        vf[k] = vv;
+    }
+    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < (int)(n & 3)) {
         const int64_t k = (n4 << 2) + threadIdx.x;
-        float *wf = reinterpret_cast<float *>(w);
-        float *mf = reinterpret_cast<float *>(m);
-        float *vf = reinterpret_cast<float *>(v);
-        const float *gf = reinterpret_cast<const float *>(g);
         float ww = wf[k], mm = mf[k], vv = vf[k];
         adamw_elem(ww, gf[k], mm, vv, s, h);
         wf[k] = ww;
@@ -389,21 +403,23 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *
     }
 }
 
-// a3 after grad_norm_final.
+// a3 after grad_norm_final. w, g, m, v point `head` (0-63) elements past the
+// arrays' starts, at 16-byte boundaries; n counts from there.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
     f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, const ClipScalars *__restrict__ sc, StepScalars h) {
-    update_body<false>(w, g, m, v, n, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), h,
+    f32x4 *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
+    StepScalars h) {
+    update_body<false>(w, g, m, v, n, head, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), h,
                        nullptr);
 }
 
 // a2 + a3 in one kernel (small n).
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
     f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, const double *__restrict__ partials, int nparts, float clip,
-    ClipScalars *__restrict__ sc_out, StepScalars h) {
+    f32x4 *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
+    float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true>(w, g, m, v, n, partials, nparts, clip, sc_out, h, lds);
+    update_body<true>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
 }
 
 // a3 for arrays that are not all 16-byte aligned: same arithmetic per element.
@@ -435,12 +451,13 @@ __global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restri
 
 // The pages' third clip kernel on its own, for callers that need the clipped
 // gradient itself: g *= s in place (skipped when the norm is not finite). Same
-// float32 product as the update's g * s. Lanes past the end re-read the last
-// vector and discard it (the host guarantees n >= 4); the last block also
-// scales the n % 4 trailing elements. FOLD as in update_body: the record from
+// float32 product as the update's g * s. g points `head` (0-63) elements past
+// the array's start, at a 16-byte boundary, and n counts from there. Lanes past the end re-read the last vector and discard it (the host
+// guarantees n >= 4); block 0 also scales the head elements and the last
+// block the n % 4 trailing ones. FOLD as in update_body: the record from
 // grad_norm_final, or the final reduction at the head of every block.
 template <bool FOLD>
-__device__ __forceinline__ void scale_body(f32x4 *__restrict__ g, int64_t n,
+__device__ __forceinline__ void scale_body(f32x4 *__restrict__ g, int64_t n, int head,
                                            const double *__restrict__ partials, int nparts,
                                            float clip, ClipScalars *__restrict__ sc, double *lds) {
     const int64_t n4 = n >> 2;
@@ -462,24 +479,28 @@ __device__ __forceinline__ void scale_body(f32x4 *__restrict__ g, int64_t n,
         for (int k = 0; k < 4; ++k) x[k] = x[k] * s;
         __builtin_nontemporal_store(x, g + i);
     }
-    const int rem = (int)(n & 3);
-    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < rem) {
-        float *gf = reinterpret_cast<float *>(g);
+    float *gf = reinterpret_cast<float *>(g);
+    if (blockIdx.x == 0 && (int)threadIdx.x < head) {  // indices -head .. -1
+        const int64_t k = (int64_t)threadIdx.x - head;
+        gf[k] = gf[k] * s;
+    }
+    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < (int)(n & 3)) {
         const int64_t k = (n4 << 2) + threadIdx.x;
         gf[k] = gf[k] * s;
     }
 }
 
 __global__ __launch_bounds__(kUpdThreads) void grad_scale_vec(f32x4 *__restrict__ g, int64_t n,
+                                                              int head,
                                                               const ClipScalars *__restrict__ sc) {
-    scale_body<false>(g, n, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), nullptr);
+    scale_body<false>(g, n, head, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), nullptr);
 }
 
 __global__ __launch_bounds__(kUpdThreads) void grad_scale_vec_fold(
-    f32x4 *__restrict__ g, int64_t n, const double *__restrict__ partials, int nparts, float clip,
-    ClipScalars *__restrict__ sc_out) {
+    f32x4 *__restrict__ g, int64_t n, int head, const double *__restrict__ partials, int nparts,
+    float clip, ClipScalars *__restrict__ sc_out) {
     __shared__ double lds[kUpdThreads / kWave];
-    scale_body<true>(g, n, partials, nparts, clip, sc_out, lds);
+    scale_body<true>(g, n, head, partials, nparts, clip, sc_out, lds);
 }
 
 __global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, int64_t n,
@@ -637,12 +658,27 @@ int64_t norm_nt_limit4(int64_t n) {
     return n4 > tail4 ? n4 - tail4 : 0;
 }
 
+// Elements before the body the vector kernels take: up to the next 256-byte
+// boundary of p (0-63), so that the body's waves cover whole cache lines;
+// when fewer than 4 elements would follow it, up to the next 16-byte boundary
+// (0-3). -1 when p is not 4-byte aligned or neither leaves 4 elements: the
+// vector kernels then do not apply.
+int head_of(const void *p, int64_t n) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p) & 255u;
+    if (a & 3u) return -1;
+    const int h = (int)((256u - a) & 255u) / 4;
+    if (n - h >= 4) return h;
+    const int h16 = h & 3;
+    return n - h16 >= 4 ? h16 : -1;
+}
+
 // a1 alone. ev0 / ev1 (optional, profiling) take the kernel's start / end.
 void launch_partial(const float *g, int64_t n, float gscale, Workspace *ws, hipStream_t stream,
                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+    const int head = head_of(g, n);
     hipExtLaunchKernelGGL(grad_norm_partial, dim3(norm_blocks(n)), dim3(kNormThreads), 0, stream,
-                          ev0, ev1, 0, g, n, aligned16(g) ? 1 : 0, norm_nt_limit4(n), gscale,
-                          ws->partials);
+                          ev0, ev1, 0, g, n, head, norm_nt_limit4(head >= 0 ? n - head : n),
+                          gscale, ws->partials);
 }
 
 // a1 + a2. ev (optional, profiling): ev[0] takes the partial kernel's start,
@@ -656,8 +692,13 @@ int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
-bool all_aligned16(const void *a, const void *b, const void *c, const void *d) {
-    return aligned16(a) && aligned16(b) && aligned16(c) && aligned16(d);
+// The head for w, g, m and v: w's (its body then starts on a 256-byte
+// boundary), provided the four lie equally far from a 16-byte boundary, so
+// that all four bodies are 16-byte aligned; -1 otherwise.
+int common_head(const void *w, const void *g, const void *m, const void *v, int64_t n) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(w) & 15u;
+    const auto same = [a](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == a; };
+    return (same(g) && same(m) && same(v)) ? head_of(w, n) : -1;
 }
 
 // Whether the vector kernels do the final reduction themselves (two launches)
@@ -665,31 +706,34 @@ bool all_aligned16(const void *a, const void *b, const void *c, const void *d) {
 // costs more than the reduction at the head of every wave.
 bool fold_final(int64_t n) { return n <= (int64_t)RCS_FOLD_MAX_N; }
 
-// The whole step a1..a3. Vector form (16-byte aligned arrays, n >= 4): the
-// partial kernel, [grad_norm_final,] the update kernel. Otherwise: partial,
-// final, scalar update.
+// The whole step a1..a3. Vector form (w, g, m, v equally far from a 16-byte
+// boundary, at least 4 elements past the head): the partial kernel,
+// [grad_norm_final,] the update kernel on the aligned body, which also takes
+// the head elements. Otherwise: partial, final, scalar update.
 // ev (optional, profiling): ev[0] / ev[1] take the start of the partial kernel
 // and the end of the last norm kernel, ev[2] / ev[3] the update's start / end.
 int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float clip,
                 const StepScalars &h, Workspace *ws, hipStream_t stream, hipEvent_t *ev) {
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-    if (n >= 4 && all_aligned16(w, g, m, v)) {
-        const int64_t blocks = ((n >> 2) + kUpdThreads - 1) / kUpdThreads;
-        f32x4 *w4 = reinterpret_cast<f32x4 *>(w), *m4 = reinterpret_cast<f32x4 *>(m);
-        f32x4 *v4 = reinterpret_cast<f32x4 *>(v);
-        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(g);
+    const int head = common_head(w, g, m, v, n);
+    if (head >= 0) {
+        const int64_t nb = n - head;  // elements from the 16-byte boundary on
+        const int64_t blocks = ((nb >> 2) + kUpdThreads - 1) / kUpdThreads;
+        f32x4 *w4 = reinterpret_cast<f32x4 *>(w + head), *m4 = reinterpret_cast<f32x4 *>(m + head);
+        f32x4 *v4 = reinterpret_cast<f32x4 *>(v + head);
+        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(g + head);
         if (fold_final(n)) {
             launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr,
                            ev ? ev[1] : nullptr);
             hipExtLaunchKernelGGL(adamw_update_vec_fold, dim3((unsigned)blocks),
-                                  dim3(kUpdThreads), 0, stream, e2, e3, 0, w4, g4, m4, v4, n,
-                                  (const double *)ws->partials, norm_blocks(n), clip, ws->scalars,
-                                  h);
+                                  dim3(kUpdThreads), 0, stream, e2, e3, 0, w4, g4, m4, v4, nb,
+                                  head, (const double *)ws->partials, norm_blocks(n), clip,
+                                  ws->scalars, h);
         } else {
             const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
             if (rc != RCS_OK) return rc;
             hipExtLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads),
-                                  0, stream, e2, e3, 0, w4, g4, m4, v4, n,
+                                  0, stream, e2, e3, 0, w4, g4, m4, v4, nb, head,
                                   (const ClipScalars *)ws->scalars, h);
         }
     } else {
@@ -822,19 +866,22 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream) {
     if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
     Workspace *ws = nullptr;
     if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
-    if (n >= 4 && aligned16(g)) {  // partial, [final,] the vector scale kernel
-        const dim3 grid((unsigned)(((n >> 2) + kUpdThreads - 1) / kUpdThreads));
+    const int head = head_of(g, n);
+    if (head >= 0) {  // partial, [final,] the vector scale kernel on the aligned body
+        const int64_t nb = n - head;
+        const dim3 grid((unsigned)(((nb >> 2) + kUpdThreads - 1) / kUpdThreads));
+        f32x4 *g4 = reinterpret_cast<f32x4 *>(g + head);
         if (fold_final(n)) {
             launch_partial(g, n, 1.0f, ws, stream);
-            hipLaunchKernelGGL(grad_scale_vec_fold, grid, dim3(kUpdThreads), 0, stream,
-                               reinterpret_cast<f32x4 *>(g), n, (const double *)ws->partials,
-                               norm_blocks(n), clip, ws->scalars);
+            hipLaunchKernelGGL(grad_scale_vec_fold, grid, dim3(kUpdThreads), 0, stream, g4, nb,
+                               head, (const double *)ws->partials, norm_blocks(n), clip,
+                               ws->scalars);
         } else {
             if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
-            hipLaunchKernelGGL(grad_scale_vec, grid, dim3(kUpdThreads), 0, stream,
-                               reinterpret_cast<f32x4 *>(g), n, (const ClipScalars *)ws->scalars);
+            hipLaunchKernelGGL(grad_scale_vec, grid, dim3(kUpdThreads), 0, stream, g4, nb, head,
+                               (const ClipScalars *)ws->scalars);
         }
-    } else {  // unaligned g or n < 4: partial, final, scalar scale
+    } else {  // g not 4-byte aligned or too short: partial, final, scalar scale
         if ((rc = launch_norm(g, n, 1.0f, clip, ws, stream)) != RCS_OK) return rc;
         int64_t blocks = (n + 255) / 256;
         if (blocks > 65536) blocks = 65536;

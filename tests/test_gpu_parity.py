@@ -163,21 +163,39 @@ def test_update_parity_ragged_sizes(dev, n):
     _run_parity(dev, wl, 3, n=n, scale=50.0)
 
 
-@pytest.mark.parametrize("offset", [1, 3])
-def test_update_parity_unaligned_scalar_path(dev, offset):
+# (offsets of w, g, m, v in elements past a 512-byte allocation start, n).
+# Offsets equal modulo 4 take the vector kernels: the head runs to w's next
+# 256-byte boundary (64 - offset elements: bodies of exactly 4 and 7 behind a
+# 63-element head, head and tail in one block), or to the next 16-byte one when
+# fewer than 4 elements would follow (heads of 1-3, bodies of 4, 5 and 7); g, m
+# and v may sit at other 256-byte phases (1, 5, 9, 65). Both final-reduction
+# forms. Offsets unequal modulo 4, and views too short for either head, take
+# the scalar kernels.
+UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3), 50_001),
+                   ((1, 1, 1, 1), 67), ((1, 1, 1, 1), 70), ((2, 2, 2, 2), 66),
+                   ((3, 3, 3, 3), 5), ((3, 3, 3, 3), 6), ((1, 1, 1, 1), 7), ((2, 2, 2, 2), 9),
+                   ((1, 5, 9, 65), 50_001), ((4, 8, 12, 0), 4099),
+                   ((1, 1, 1, 1), 8_388_611), ((3, 3, 3, 3), 8_388_608),
+                   ((1, 2, 0, 3), 50_001), ((0, 0, 0, 1), 4099), ((2, 2, 2, 2), 5)]
+
+
+@pytest.mark.parametrize("offs,n", UNALIGNED_CASES)
+def test_update_parity_unaligned_views(dev, offs, n):
     wl = workloads.WORKLOADS["flat262k"]
-    n = 50_001
-    mk = lambda: torch.zeros(n + offset, device=dev)  # noqa: E731
-    W, G, M, V = mk(), mk(), mk(), mk()
-    w, g, m, v = W[offset:], G[offset:], M[offset:], V[offset:]
+    W, G, M, V = (torch.zeros(n + o, device=dev) for o in offs)
+    w, g, m, v = (X[o:] for X, o in zip((W, G, M, V), offs))
     w.copy_(workloads.init_params(wl, device=dev, n=n))
     ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
     for t in (1, 2, 3):
         g.copy_(workloads.grads(wl, t, device=dev, n=n)).mul_(10.0)
         rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
-        oracle.adamw_clip_step(ow, _host(g).copy(), om, ov, t, wl.lr, wl.wd, wl.clip)
-        torch.cuda.synchronize()
-        _check_state(w, m, v, ow, om, ov, f"unaligned offset={offset} t={t}")
+        gn = _gpu_norm()
+        rc, on = oracle.adamw_clip_step(ow, _host(g).copy(), om, ov, t, wl.lr, wl.wd, wl.clip)
+        assert rc == oracle.OK and abs(gn - on) <= NORM_RTOL * on, (offs, n, t, gn, on)
+        _check_state(w, m, v, ow, om, ov, f"offsets={offs} n={n} t={t}")
+    # the elements just outside the views are never written
+    for X, o in zip((W, G, M, V), offs):
+        assert (X[:o] == 0).all()
 
 
 def test_update_parity_andrea12m(dev):
@@ -240,16 +258,18 @@ def test_step_norm_same_bits_as_final_kernel(dev, n):
         _check_state(w, m, v, ow, om, ov, f"n={n} t={t}")
 
 
-@pytest.mark.parametrize("n,off", [(10_000, 0), (5_000_001, 0), (10_000, 1), (3, 0)])
-def test_nonfinite_norm_skips_update(dev, n, off):
-    """Both update forms skip: the vector kernel (aligned, n >= 4) and the
-    scalar one after the final kernel (unaligned views, n < 4)."""
+@pytest.mark.parametrize("n,off,goff", [(10_000, 0, 0), (5_000_001, 0, 0), (10_000, 1, 1),
+                                         (10_000, 1, 2), (3, 0, 0)])
+def test_nonfinite_norm_skips_update(dev, n, off, goff):
+    """Every update form skips: the vector kernels (equal offsets, with and
+    without a peeled head, both final-reduction forms) and the scalar one after
+    the final kernel (unequal offsets, n < 4)."""
     w = workloads.custom(104, n + off, 0.02, device=dev)[off:]
     m = workloads.custom(105, n + off, 0.01, device=dev)[off:]
     v = workloads.custom(106, n + off, 0.01, device=dev)[off:].abs_()
     before = [_host(x).copy() for x in (w, m, v)]
     for bad in (float("inf"), float("nan")):
-        g = workloads.custom(107, n + off, 1.0, device=dev)[off:]
+        g = workloads.custom(107, n + goff, 1.0, device=dev)[goff:]
         g[min(777, n - 1)] = bad
         rcs.adamw_clip_step(w, g, m, v, 4, 3e-3, 0.01, 1.0)
         norm = _gpu_norm()
@@ -524,7 +544,9 @@ def test_edge_scalars_and_values(dev, case):
 
 def test_randomized_cases_against_oracle(dev):
     """160 seeded random cases, two updates each: sizes 1 .. ~70,000 (both
-    launch forms, ragged tails), unaligned views (scalar kernels), t up to
+    launch forms, ragged tails), views 0-79 elements past an allocation's
+    start (equal offsets modulo 4: vector kernels with a peeled head; else
+    scalar), t up to
     2^31 - 2, lr, wd, clip and gradient scales over many decades (clipped and
     unclipped), micro-batch scales; the norm and w, m, v against the oracle at
     the usual bar."""
@@ -532,7 +554,8 @@ def test_randomized_cases_against_oracle(dev):
     clipped = unclipped = 0
     for case in range(160):
         n = int(np.exp(rng.uniform(0.0, np.log(70_000))))
-        off = int(rng.choice([0, 0, 1, 2, 3]))
+        off = int(rng.choice([0, 0, 1, 2, 3, int(rng.integers(4, 80))]))
+        offs = [off] * 4 if rng.random() < 0.8 else [int(x) for x in rng.integers(0, 80, 4)]
         t = int(min(np.exp(rng.uniform(0.0, np.log(2**31 - 2))), 2**31 - 2))
         lr = float(10 ** rng.uniform(-6, -1))
         wd = float(rng.choice([0.0, rng.uniform(0.0, 0.2)]))
@@ -542,11 +565,11 @@ def test_randomized_cases_against_oracle(dev):
         base = 1000 + 4 * case
         arrs = []
         for k, sd in enumerate((0.02, sigma, 0.01, 0.01)):
-            x = workloads.custom(base + k, n + off, sd, device=dev)[off:]
+            x = workloads.custom(base + k, n + offs[k], sd, device=dev)[offs[k]:]
             arrs.append(x.square_() if k == 3 else x)
         w, g, m, v = arrs
         ow, og, om, ov = (_host(x).copy() for x in arrs)
-        ctx = f"case {case}: n={n} off={off} t={t} lr={lr:.3g} wd={wd:.3g} clip={clip:.3g} " \
+        ctx = f"case {case}: n={n} offs={offs} t={t} lr={lr:.3g} wd={wd:.3g} clip={clip:.3g} " \
               f"sigma={sigma:.3g} scale={scale:.3g}"
         for tt in (t, t + 1):
             rcs.adamw_clip_step_accum(w, g, m, v, tt, lr, wd, clip, scale)
@@ -639,8 +662,10 @@ def test_host_threads_each_on_its_own_stream(dev):
 
 @pytest.mark.parametrize("n,offset,sigma", [(1, 0, 5.0), (7, 0, 5.0), (262_147, 0, 0.01),
                                             (1_000_003, 0, 1.0), (100_001, 1, 1.0),
-                                            (8_388_611, 0, 1e-4), (12_800_000, 0, 1e-4),
-                                            (124_356_866, 0, 1e-4)])
+                                            (100_001, 2, 1.0), (7, 1, 5.0), (6, 1, 5.0),
+                                            (67, 1, 5.0), (70, 1, 5.0),
+                                            (8_388_611, 0, 1e-4), (8_388_613, 3, 1e-4),
+                                            (12_800_000, 0, 1e-4), (124_356_866, 0, 1e-4)])
 def test_grad_clip_inplace_parity(dev, n, offset, sigma):
     base = workloads.custom(600, n + offset, sigma, device=dev)
     g = base[offset:]
@@ -650,6 +675,9 @@ def test_grad_clip_inplace_parity(dev, n, offset, sigma):
     rc, on = oracle.clip_grads(og, 1.0)
     assert rc == oracle.OK and abs(gn - on) <= NORM_RTOL * on
     assert max_ulp(_host(g), og) <= ULP_TOL
+    if offset:
+        assert (bits(_host(base[:offset])) == bits(_host(
+            workloads.custom(600, n + offset, sigma, device=dev)[:offset]))).all()
 
 
 def test_grad_clip_inplace_nonfinite_untouched(dev):
