@@ -259,7 +259,8 @@ int rcs_signals_poll(void);
  * rcs_ckpt_writer_wait: blocks until no write is in flight and returns the
  * status of the last finished one; path_out (optional, path_cap bytes)
  * receives the path it wrote. Both are reported once: a second wait returns
- * RCS_OK and "".
+ * RCS_OK and "". A path_cap too small for the path returns RCS_EINVAL and
+ * leaves the status and path to the next wait.
  * rcs_ckpt_writer_destroy: waits, stops the worker, frees everything; returns
  * the status of the last write not yet reported. NULL is a no-op.
  */

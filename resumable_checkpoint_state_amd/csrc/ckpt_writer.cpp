@@ -148,14 +148,13 @@ int rcs_ckpt_writer_wait(rcs_ckpt_writer *wr, char *path_out, int64_t path_cap) 
     if (wr == nullptr) return RCS_EINVAL;
     std::unique_lock<std::mutex> lk(wr->mu);
     wr->cv.wait(lk, [wr] { return !wr->pending; });
+    // a path_out too small for the path reports nothing and leaves both pending
+    if (path_out != nullptr && path_cap < (int64_t)wr->path.size() + 1) return RCS_EINVAL;
     const int rc = wr->status;
     wr->status = RCS_OK;
     std::string path;
     path.swap(wr->path);  // reported once, like the status
-    if (path_out != nullptr) {
-        if (path_cap < (int64_t)path.size() + 1) return rc != RCS_OK ? rc : RCS_EINVAL;
-        memcpy(path_out, path.c_str(), path.size() + 1);
-    }
+    if (path_out != nullptr) memcpy(path_out, path.c_str(), path.size() + 1);
     return rc;
 }
 

@@ -147,8 +147,12 @@ int main(int argc, char **argv) {
             std::this_thread::yield();
         }
     });
-    std::vector<std::vector<unsigned char>> expect(21);
-    for (int step = 1; step <= 20; ++step) {
+    std::vector<std::vector<unsigned char>> expect(22);
+    for (int step = 1; step <= 21; ++step) {
+        if (step == 21) {  // the concurrent waiter has stopped
+            done = true;
+            waiter.join();
+        }
         for (int64_t i = 0; i < n; ++i) {
             w[i] = (float)(step * 1000 + i);
             m[i] = (float)(step + 0.5 * i);
@@ -165,18 +169,20 @@ int main(int argc, char **argv) {
         // the caller may change the state at once; the file must hold the state at submit
         for (int64_t i = 0; i < n; ++i) w[i] = -1.0f;
     }
-    done = true;
-    waiter.join();
-    char path[4096];
+    // a path buffer too small for the path reports nothing; the next wait does
+    char path[4096], small[4];
+    CHECK(rcs_ckpt_writer_wait(wr, small, sizeof small) == RCS_EINVAL);
     CHECK(rcs_ckpt_writer_wait(wr, path, sizeof path) == RCS_OK);
+    CHECK(std::strstr(path, "step_000021.bin") != nullptr);
+    CHECK(rcs_ckpt_writer_wait(wr, path, sizeof path) == RCS_OK && path[0] == '\0');
     CHECK(rcs_ckpt_writer_destroy(wr) == RCS_OK);
-    for (int step = 19; step <= 20; ++step) {
+    for (int step = 20; step <= 21; ++step) {
         char name[64];
         std::snprintf(name, sizeof name, "/step_%06d.bin", step);
         CHECK(read_file(dir + name) == expect[step]);
     }
     char old[64];
-    std::snprintf(old, sizeof old, "/step_%06d.bin", 18);
+    std::snprintf(old, sizeof old, "/step_%06d.bin", 19);
     CHECK(read_file(dir + old).empty());  // rotated away (keep = 2)
 
     // a failed write is reported by wait
