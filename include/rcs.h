@@ -203,7 +203,8 @@ int ckpt_pack_wait(const float *snapshot);
  * buf_bytes. Writes <dir>/step_%06d.bin.tmp, fsyncs it, renames it to
  * <dir>/step_%06d.bin (atomic on POSIX) and fsyncs the directory, so a crash
  * leaves either the old set of files or the new complete file. The final path
- * is copied to path_out (if not NULL; RCS_EINVAL if path_cap is too small).
+ * is copied to path_out (if not NULL; RCS_EINVAL, before anything is
+ * written, if path_cap is too small).
  * ckpt_file_size: size in bytes of a regular file, or RCS_ENOENT.
  * ckpt_file_read: reads a whole file into host_buf; its size must equal
  * buf_bytes (RCS_ESIZE) and its header must be consistent (RCS_EHEADER).
@@ -211,7 +212,8 @@ int ckpt_pack_wait(const float *snapshot);
  * step_<digits>.bin matching the header's step, header consistent with the
  * size); temporaries and malformed files are skipped; RCS_ENOENT if none.
  * ckpt_file_rotate: keeps the `keep` newest valid step files, deletes the
- * older ones and any step_*.bin.tmp leftovers; returns how many were removed.
+ * older ones and any step_*.bin.tmp leftovers (so no other writer may be
+ * writing into dir at the time); returns how many were removed.
  */
 int ckpt_file_write(const char *dir, const void *host_buf, int64_t buf_bytes, char *path_out,
                     int64_t path_cap);

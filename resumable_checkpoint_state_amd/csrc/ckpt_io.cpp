@@ -181,6 +181,8 @@ int ckpt_file_write(const char *dir, const void *host_buf, int64_t buf_bytes, ch
     int rc = check_header(b, buf_bytes, &step, &n);
     if (rc != RCS_OK) return rc;
     const std::string final_path = std::string(dir) + "/" + step_name(step);
+    // a path_out too small for the path is refused before anything is written
+    if (path_out != nullptr && path_cap < (int64_t)final_path.size() + 1) return RCS_EINVAL;
     if ((rc = atomic_write(final_path, b, buf_bytes)) != RCS_OK) return rc;
     return copy_path(final_path, path_out, path_cap);
 }

@@ -40,7 +40,9 @@ int main(int argc, char **argv) {
     char small[8];
     auto b = packed(50, 7);
     EXPECT(ckpt_file_write(d.c_str(), b.data(), (int64_t)b.size(), small, sizeof small) ==
-           RCS_EINVAL);  // path does not fit: file written, path refused
+           RCS_EINVAL);  // path does not fit: refused before anything is written
+    EXPECT(ckpt_file_size((d + "/step_000050.bin").c_str()) == RCS_ENOENT);
+    EXPECT(ckpt_file_write(d.c_str(), b.data(), (int64_t)b.size(), nullptr, 0) == RCS_OK);
     b.pop_back();
     EXPECT(ckpt_file_write(d.c_str(), b.data(), (int64_t)b.size(), nullptr, 0) == RCS_ESIZE);
     FILE *f = fopen((d + "/step_000060.bin").c_str(), "wb");  // truncated newer file

@@ -117,3 +117,15 @@ def test_signal_flags_are_polled_and_cleared():
     finally:
         signal.signal(signal.SIGTERM, signal.SIG_DFL)
         signal.signal(signal.SIGUSR1, signal.SIG_DFL)
+
+
+def test_short_path_buffer_refused_before_writing(tmp_path):
+    """ckpt_file_write with a path_out too small for the final path returns
+    RCS_EINVAL and leaves the directory as it was (through the C ABI)."""
+    import ctypes
+    buf = packed(7, 12)
+    small = ctypes.create_string_buffer(8)
+    rc = rcs.lib().ckpt_file_write(os.fsencode(str(tmp_path)), ctypes.c_void_p(buf.data_ptr()),
+                                   buf.numel(), small, 8)
+    assert rc == rcs.EINVAL
+    assert os.listdir(tmp_path) == []
