@@ -38,6 +38,11 @@
 //   * adamw_update_vec_fold: for n up to 8,388,608, where the step is bound
 //     by launch cost, every wave does grad_norm_final's reduction itself (the
 //     same bits) and the step is two launches instead of three.
+//   * Arrays that start off a 16-byte boundary, all four by the same amount
+//     (views into a flat buffer), keep the vector kernels: block 0 takes the
+//     0-63 elements before w's next 256-byte boundary one per lane, and the
+//     waves stream whole cache lines from there. Arrays at different 16-byte
+//     phases take scalar kernels with the same arithmetic.
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
