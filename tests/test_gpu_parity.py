@@ -79,9 +79,15 @@ def test_norm_parity_sizes(dev, n):
     assert abs(got - ref) <= NORM_RTOL * ref, (n, got, ref)
 
 
-@pytest.mark.parametrize("offset", [1, 2, 3])
-def test_norm_parity_unaligned(dev, offset):
-    n = 100_003
+# (elements past a 512-byte allocation start, n): heads of 63, 62, 61, 47 and 1
+# elements before g's next 256-byte boundary; 16-byte heads when fewer than 4
+# elements would follow it (n = 66: head 3, body 63); the scalar loop when even
+# that leaves fewer than 4 (n = 6); several grid-stride passes with the
+# cache-allocating tail (n = 40,000,003).
+@pytest.mark.parametrize("offset,n", [(1, 100_003), (2, 100_003), (3, 100_003), (17, 100_003),
+                                      (63, 100_003), (1, 66), (1, 67), (1, 6),
+                                      (2, 40_000_003)])
+def test_norm_parity_unaligned(dev, offset, n):
     base = workloads.custom(101, n + offset, 1.0, device=dev)
     g = base[offset:]
     out = rcs.grad_global_norm(g)
