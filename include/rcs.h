@@ -12,7 +12,9 @@
  * The only device memory the library owns is a per-(device, stream)
  * workspace of about 2.3 KiB (256 per-block float64 partial sums and the clip
  * scalars). It is allocated by rcs_init or on the first call that needs it,
- * never inside a later call, and lives until the process ends. (The
+ * never inside a later call, and lives until the process ends. Under
+ * hipStreamPerThread, which is a different stream in every host thread, each
+ * calling thread gets its own workspace (rcs_init from that thread). (The
  * asynchronous pack also keeps two HIP events per snapshot buffer, and the
  * instrumentation its events while enabled. An rcs_ckpt_writer, created and
  * destroyed explicitly, owns its snapshot, host buffer, stream and thread.)

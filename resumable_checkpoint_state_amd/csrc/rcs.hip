@@ -557,6 +557,9 @@ __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restr
 
 }  // namespace
 
+#include <thread>
+#include <tuple>
+
 #include "rcs_internal.h"
 
 namespace {
@@ -568,7 +571,10 @@ struct Workspace {
 };
 
 std::mutex g_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Keyed by device and stream; hipStreamPerThread names a different stream in
+// every host thread, so under that handle the thread is part of the key.
+using WsKey = std::tuple<int, hipStream_t, std::thread::id>;
+std::map<WsKey, Workspace> g_ws;
 
 // Per snapshot buffer: `ready` is recorded on the compute stream after the
 // snapshot kernel, `copied` on the copy stream after the device-to-host copy.
@@ -593,8 +599,9 @@ struct Profile {
 int get_workspace(hipStream_t stream, Workspace **out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
+    const WsKey key(dev, stream,
+                    stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id());
     std::lock_guard<std::mutex> lk(g_mu);
-    auto key = std::make_pair(dev, stream);
     auto it = g_ws.find(key);
     if (it == g_ws.end()) {
         void *p = nullptr;

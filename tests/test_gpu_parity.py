@@ -617,11 +617,17 @@ def test_two_streams_have_separate_workspaces(dev):
     _check_state(*B, *oB, "stream B")
 
 
-def test_host_threads_each_on_its_own_stream(dev):
+HIP_STREAM_PER_THREAD = 2  # the hipStreamPerThread handle
+
+
+@pytest.mark.parametrize("mode", ["own_streams", "per_thread_handle"])
+def test_host_threads_each_on_its_own_stream(dev, mode):
     """Four host threads, each with its own stream and parameters, call the
     library at once (the ctypes calls release the GIL, so the C library sees
     concurrent calls, first-use workspace creation included); every result is
-    bit-identical to the same updates run one after another."""
+    bit-identical to the same updates run one after another. per_thread_handle:
+    every thread passes hipStreamPerThread, one handle that names a different
+    stream in each thread, so each thread needs a workspace of its own."""
     import threading
     sizes = [262_147, 1_000_003, 4099, 3_000_001]
     steps = 10
@@ -642,6 +648,15 @@ def test_host_threads_each_on_its_own_stream(dev):
     def work(k):
         try:
             torch.cuda.set_device(0)
+            if mode == "per_thread_handle":
+                start.wait()
+                w, m, v = states[k]
+                for t in range(1, steps + 1):
+                    rcs.adamw_clip_step(w, grads[k][t - 1], m, v, t, 3e-3, 0.01, 1.0,
+                                        stream=HIP_STREAM_PER_THREAD)
+                norms[k] = rcs.last_grad_norm(stream=HIP_STREAM_PER_THREAD)
+                torch.cuda.synchronize()
+                return
             with torch.cuda.stream(streams[k]):
                 start.wait()
                 w, m, v = states[k]
