@@ -51,7 +51,9 @@ enum rcs_status {
 const char *rcs_strerror(int status);
 
 /* Allocates the workspace of (device, stream) ahead of time so that no later
- * call allocates. Optional. */
+ * call allocates. Optional; needed before capturing adamw_clip_step (or the
+ * norm and clip calls) on that stream into a graph: the capture then holds
+ * only the kernels, with t and the hyper-parameters fixed at capture. */
 int rcs_init(int device, hipStream_t stream);
 
 /*

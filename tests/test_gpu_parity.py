@@ -771,3 +771,41 @@ def test_init_and_last_norm_rejections(dev):
         rcs.grad_global_norm(g)
         got = float(rcs.last_grad_norm().cpu())
     assert abs(got - oracle.grad_norm(_host(g))) <= NORM_RTOL * got
+
+
+@pytest.mark.parametrize("n", [1_000_003, 12_800_003])
+def test_step_captured_in_a_graph_replays_like_eager(dev, n):
+    """A caller may capture the step into its own graph once the stream's
+    workspace exists (rcs_init): the capture then holds only the kernels (two
+    launches at 1,000,003 elements, three at 12,800,003; no allocation, no
+    memset). Each replay, with eager work and synchronizations between
+    replays, gives w, m, v and the norm bit-identical to the same update run
+    eagerly (t and the hyper-parameters are frozen at capture)."""
+    s = torch.cuda.Stream()
+    rcs.init(stream=s)
+    g = workloads.custom(900, n, 0.05, device=dev)
+    w0 = workloads.custom(901, n, 0.02, device=dev)
+    m0 = workloads.custom(902, n, 0.01, device=dev)
+    v0 = workloads.custom(903, n, 0.01, device=dev).square_()
+    w, m, v = w0.clone(), m0.clone(), v0.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        rcs.adamw_clip_step(w, g, m, v, 7, 3e-3, 0.01, 1.0)
+    torch.cuda.synchronize()
+    for k in range(3):
+        scale = 1.0 + 0.5 * k
+        w.copy_(w0 * scale)
+        m.copy_(m0)
+        v.copy_(v0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_norm = float(rcs.last_grad_norm(stream=s).cpu())
+        we, me, ve = w0 * scale, m0.clone(), v0.clone()
+        rcs.adamw_clip_step(we, g, me, ve, 7, 3e-3, 0.01, 1.0)
+        eager_norm = float(rcs.last_grad_norm().cpu())
+        torch.cuda.synchronize()
+        for a, b in ((w, we), (m, me), (v, ve)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (n, k)
+        assert got_norm == eager_norm, (n, k, got_norm, eager_norm)
