@@ -135,6 +135,18 @@ int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t st
 int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream);
 
 /*
+ * Sets g[0..n) to +0.0f: the reset of the gradient buffer after the
+ * optimizer step in the backprop lesson's accumulation loop (under
+ * "accumulation over micro-batches": backward adds into one buffer with +=,
+ * so it must be cleared before the next step's first micro-batch; the
+ * resume page's update order likewise starts with zeroing the gradients).
+ * g: device float32[n], n 1 .. RCS_MAX_N; 4 bytes written per element, with
+ * streaming 16-byte stores from g's next 256-byte boundary on. A kernel, not
+ * a memset, so it may be captured into a graph. Asynchronous on stream.
+ */
+int grad_zero(float *g, int64_t n, hipStream_t stream);
+
+/*
  * Copies the pre-clip norm computed by the most recent adamw_clip_step,
  * adamw_clip_step_accum, grad_clip_inplace or grad_global_norm on this stream into norm_out (device or pinned host
  * float64), in stream order. The resume lesson records this norm before the

@@ -19,7 +19,7 @@ from ._build import LIB as LIB_PATH
 from ._build import build
 
 __all__ = [
-    "RcsError", "adamw_clip_step", "adamw_clip_step_accum", "grad_clip_inplace", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
+    "RcsError", "adamw_clip_step", "adamw_clip_step_accum", "grad_clip_inplace", "grad_zero", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
     "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read", "fp32_div_sqrt_probe",
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
     "ckpt_pack_async", "ckpt_pack_wait", "CkptWriter", "StepFileCheckpointer",
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.adamw_clip_step_accum.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, f32, vp]
     L.adamw_clip_step_accum.restype = ctypes.c_int
     L.grad_clip_inplace.argtypes = [f32p, i64, f32, vp]
+    L.grad_zero.argtypes = [f32p, i64, vp]
+    L.grad_zero.restype = ctypes.c_int
     L.grad_clip_inplace.restype = ctypes.c_int
     L.ckpt_snapshot_bytes.argtypes = [i64]
     L.ckpt_snapshot_bytes.restype = i64
@@ -188,6 +190,11 @@ def grad_clip_inplace(g, clip: float, stream=None) -> None:
     """g *= clip/||g|| in place when ||g|| > clip (the global clip on its own)."""
     _check(lib().grad_clip_inplace(_dev_f32(g, "g"), g.numel(), float(clip), _stream(stream)),
            "grad_clip_inplace")
+
+
+def grad_zero(g, stream=None) -> None:
+    """g = 0 in place: clears the accumulation buffer after the step."""
+    _check(lib().grad_zero(_dev_f32(g, "g"), g.numel(), _stream(stream)), "grad_zero")
 
 
 def _norm_out(out):

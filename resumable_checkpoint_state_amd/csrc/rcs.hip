@@ -508,6 +508,29 @@ __global__ __launch_bounds__(kUpdThreads) void grad_scale_vec_fold(
     scale_body<true>(g, n, head, partials, nparts, clip, sc_out, lds);
 }
 
+// Clears the gradient buffer for the next step's micro-batches (the backprop
+// lesson's accumulation loop: backward adds into one buffer, the optimizer
+// step reads it, then it is reset to zero). g points `head` (0-63) elements
+// past the array's start, at a 16-byte boundary; one 16-byte streaming store
+// per lane, block 0 also clears the head elements, the last block the n % 4
+// trailing ones. A kernel rather than a memset, so that it can sit in a
+// captured graph.
+__global__ __launch_bounds__(kUpdThreads) void grad_zero_vec(f32x4 *__restrict__ g, int64_t n,
+                                                             int head) {
+    const int64_t n4 = n >> 2;
+    const int64_t i = (int64_t)blockIdx.x * kUpdThreads + threadIdx.x;
+    if (i < n4) __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, g + i);
+    float *gf = reinterpret_cast<float *>(g);
+    if (blockIdx.x == 0 && (int)threadIdx.x < head) gf[(int64_t)threadIdx.x - head] = 0.0f;
+    if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < (int)(n & 3))
+        gf[(n4 << 2) + threadIdx.x] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void grad_zero_scalar(float *__restrict__ g, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) g[i] = 0.0f;
+}
+
 __global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, int64_t n,
                                                          const ClipScalars *__restrict__ sc) {
     if (!sc->apply) return;
@@ -903,6 +926,24 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return RCS_EHIP;
     ws->has_norm = true;
     return RCS_OK;
+}
+
+int grad_zero(float *g, int64_t n, hipStream_t stream) {
+    if (!valid_n(n)) return RCS_EINVAL;
+    int rc;
+    if ((rc = check_device_range(g, 4 * n)) != RCS_OK) return rc;
+    const int head = head_of(g, n);
+    if (head >= 0) {
+        const int64_t nb = n - head;
+        const dim3 grid((unsigned)(((nb >> 2) + kUpdThreads - 1) / kUpdThreads));
+        hipLaunchKernelGGL(grad_zero_vec, grid, dim3(kUpdThreads), 0, stream,
+                           reinterpret_cast<f32x4 *>(g + head), nb, head);
+    } else {
+        int64_t blocks = (n + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(grad_zero_scalar, dim3((unsigned)blocks), dim3(256), 0, stream, g, n);
+    }
+    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
 int last_grad_norm(hipStream_t stream, double *norm_out) {

@@ -76,6 +76,9 @@ def test_adamw_clip_step_rejects_bad_scalars(L, n, t, lr, wd, clip):
 def test_null_pointers_rejected(L):
     assert L.adamw_clip_step(None, None, None, None, 16, 1, 1e-3, 0.0, 1.0, None) == rcs.EINVAL
     assert L.grad_global_norm(None, 16, None, None) == rcs.EINVAL
+    assert L.grad_zero(None, 16, None) == rcs.EINVAL
+    assert L.grad_zero(FAKE, 0, None) == rcs.EINVAL
+    assert L.grad_zero(FAKE, 2**31, None) == rcs.EINVAL
     assert L.last_grad_norm(None, None) == rcs.EINVAL
     buf = (ctypes.c_uint8 * 20)()
     assert L.ckpt_pack(1, 1, FAKE, FAKE, FAKE, None, 20, None) == rcs.EINVAL

@@ -53,6 +53,51 @@ def test_accumulated_microbatch_step_parity(dev, n_micro, n):
             assert max_ulp(_host(a), b) <= 2, (n_micro, t, name)
 
 
+@pytest.mark.parametrize("n,offset", [(1, 0), (3, 0), (5, 0), (4099, 0), (1_000_003, 0),
+                                      (100_001, 1), (67, 1), (66, 1), (6, 1), (100_003, 17),
+                                      (12_800_003, 2)])
+def test_grad_zero_clears_exactly_the_view(dev, n, offset):
+    """grad_zero writes +0.0 to every element of the view (vector kernel with
+    heads of 1-63 elements and ragged tails, the 16-byte fallback and the
+    scalar kernel) and nothing before or after it."""
+    base = workloads.custom(950, n + offset + 5, 1.0, device=dev)
+    before = _host(base).copy()
+    rcs.grad_zero(base[offset:offset + n])
+    torch.cuda.synchronize()
+    after = _host(base)
+    assert (bits(after[offset:offset + n]) == 0).all()
+    assert (bits(after[:offset]) == bits(before[:offset])).all()
+    assert (bits(after[offset + n:]) == bits(before[offset + n:])).all()
+
+
+def test_accumulation_loop_reuses_one_buffer_with_grad_zero(dev):
+    """The backprop lesson's loop on one gradient buffer: micro-batches add
+    into it, the accumulated step reads it, grad_zero clears it for the next
+    step. Three steps of three micro-batches against the oracle fed the same
+    float32 sums."""
+    n, n_micro = 1_000_003, 3
+    wl = workloads.WORKLOADS["andrea12m"]
+    w = workloads.init_params(wl, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    scale = float(np.float32(1.0) / np.float32(n_micro))
+    g_sum = workloads.custom(299, n, 1.0, device=dev)  # stale contents from "before"
+    rcs.grad_zero(g_sum)
+    for t in (1, 2, 3):
+        og = np.zeros(n, np.float32)
+        for k in range(n_micro):
+            mb = workloads.custom(300 + 10 * t + k, n, 0.05, device=dev)
+            g_sum.add_(mb)
+            og += _host(mb)
+        rcs.adamw_clip_step_accum(w, g_sum, m, v, t, wl.lr, wl.wd, wl.clip, scale)
+        rcs.grad_zero(g_sum)
+        rc, on = oracle.adamw_clip_step_accum(ow, og, om, ov, t, wl.lr, wl.wd, wl.clip, scale)
+        assert rc == oracle.OK
+        for name, a, b in (("w", w, ow), ("m", m, om), ("v", v, ov)):
+            assert max_ulp(_host(a), b) <= 2, (t, name)
+        assert not bool(g_sum.any())
+
+
 def test_accum_with_unit_scale_equals_plain_step(dev):
     n = 100_000
     wl = workloads.WORKLOADS["flat262k"]
