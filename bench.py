@@ -414,6 +414,19 @@ def main() -> int:
     clip_s = ev0.elapsed_time(ev1) / reps / 1e3
     result["grad_clip_inplace"] = {"us": clip_s * 1e6, "GBps_12B_per_param": 12 * n / clip_s / 1e9}
 
+    # the accumulation buffer's reset after the step, 4 B/param written (on a
+    # scratch buffer: the gradient buffers keep their contents)
+    scratch = torch.empty(n, dtype=torch.float32, device=dev)
+    rcs.grad_zero(scratch, stream=stream)
+    ev0.record(stream)
+    for _ in range(reps):
+        rcs.grad_zero(scratch, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    zero_s = ev0.elapsed_time(ev1) / reps / 1e3
+    result["grad_zero"] = {"us": zero_s * 1e6, "GBps_4B_per_param": 4 * n / zero_s / 1e9}
+    del scratch
+
     if not args.no_torch_ref:
         ref = torch_reference(torch, wl, w, grads, min(args.steps, 50))
         ref["our_speedup"] = ref["us_per_step"] / (ms_step * 1e3)

@@ -141,7 +141,7 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream);
  * so it must be cleared before the next step's first micro-batch; the
  * resume page's update order likewise starts with zeroing the gradients).
  * g: device float32[n], n 1 .. RCS_MAX_N; 4 bytes written per element, with
- * streaming 16-byte stores from g's next 256-byte boundary on. A kernel, not
+ * 16-byte stores (256-lane blocks) from g's next 256-byte boundary on. A kernel, not
  * a memset, so it may be captured into a graph. Asynchronous on stream.
  */
 int grad_zero(float *g, int64_t n, hipStream_t stream);

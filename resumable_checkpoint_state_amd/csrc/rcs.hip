@@ -511,15 +511,20 @@ __global__ __launch_bounds__(kUpdThreads) void grad_scale_vec_fold(
 // Clears the gradient buffer for the next step's micro-batches (the backprop
 // lesson's accumulation loop: backward adds into one buffer, the optimizer
 // step reads it, then it is reset to zero). g points `head` (0-63) elements
-// past the array's start, at a 16-byte boundary; one 16-byte streaming store
-// per lane, block 0 also clears the head elements, the last block the n % 4
-// trailing ones. A kernel rather than a memset, so that it can sit in a
-// captured graph.
-__global__ __launch_bounds__(kUpdThreads) void grad_zero_vec(f32x4 *__restrict__ g, int64_t n,
-                                                             int head) {
+// past the array's start, at a 16-byte boundary; one 16-byte store per lane,
+// block 0 also clears the head elements, the last block the n % 4 trailing
+// ones. A pure write stream wants more lanes per block than the update: at
+// the ANDREA-120M size 256-lane blocks fill at 6.6-6.8 TB/s against 4.7 with
+// one-wave blocks (128: 6.1, 512: 6.2, 1024: 5.9; 2 vectors per lane or a
+// grid-stride loop slower still), and ordinary stores edge out streaming
+// ones (73-74 against 75-77 us). A kernel rather than a memset, so that it
+// can sit in a captured graph.
+constexpr int kZeroThreads = 256;
+__global__ __launch_bounds__(kZeroThreads) void grad_zero_vec(f32x4 *__restrict__ g, int64_t n,
+                                                              int head) {
     const int64_t n4 = n >> 2;
-    const int64_t i = (int64_t)blockIdx.x * kUpdThreads + threadIdx.x;
-    if (i < n4) __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, g + i);
+    const int64_t i = (int64_t)blockIdx.x * kZeroThreads + threadIdx.x;
+    if (i < n4) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float *gf = reinterpret_cast<float *>(g);
     if (blockIdx.x == 0 && (int)threadIdx.x < head) gf[(int64_t)threadIdx.x - head] = 0.0f;
     if (blockIdx.x == gridDim.x - 1 && (int)threadIdx.x < (int)(n & 3))
@@ -935,8 +940,8 @@ int grad_zero(float *g, int64_t n, hipStream_t stream) {
     const int head = head_of(g, n);
     if (head >= 0) {
         const int64_t nb = n - head;
-        const dim3 grid((unsigned)(((nb >> 2) + kUpdThreads - 1) / kUpdThreads));
-        hipLaunchKernelGGL(grad_zero_vec, grid, dim3(kUpdThreads), 0, stream,
+        const dim3 grid((unsigned)(((nb >> 2) + kZeroThreads - 1) / kZeroThreads));
+        hipLaunchKernelGGL(grad_zero_vec, grid, dim3(kZeroThreads), 0, stream,
                            reinterpret_cast<f32x4 *>(g + head), nb, head);
     } else {
         int64_t blocks = (n + 255) / 256;
