@@ -80,16 +80,16 @@
 #ifndef RCS_UPD_NT
 #define RCS_UPD_NT 1
 #endif
-// Bytes at the end of g that the norm pass reads with ordinary (cache-
-// allocating) loads so that the update, which reads g again right after,
-// finds them in the last-level cache; the rest is read with streaming loads.
-// A negative value reads all of g with ordinary loads.
 // Largest n whose step folds the final norm reduction into the update kernel
 // (measured: folding saves 1.7-2.4 us per step up to 8,388,608 elements and
 // costs 4.8 us at 16,777,216 and 23 us at 124,356,864).
 #ifndef RCS_FOLD_MAX_N
 #define RCS_FOLD_MAX_N 8388608
 #endif
+// Bytes at the end of g that the norm pass reads with ordinary (cache-
+// allocating) loads so that the update, which reads g again right after,
+// finds them in the last-level cache; the rest is read with streaming loads.
+// A negative value reads all of g with ordinary loads.
 #ifndef RCS_NORM_CACHED_TAIL_BYTES
 #define RCS_NORM_CACHED_TAIL_BYTES (320LL << 20)
 #endif
