@@ -61,13 +61,13 @@ class ShardManifest:
 
     @staticmethod
     def from_json(text: str) -> "ShardManifest":
-        d = json.loads(text)
-        try:
+        try:  # bad JSON, missing keys, wrong types and non-numbers all refuse the load
+            d = json.loads(text)
             shards = [ShardEntry(**s) for s in d["shards"]]
             return ShardManifest(world_size=int(d["world_size"]), step=int(d["step"]),
                                  wall_clock_seconds=float(d["wall_clock_seconds"]),
                                  shards=shards, schema_version=int(d["schema_version"]))
-        except (KeyError, TypeError) as e:
+        except (KeyError, TypeError, ValueError) as e:
             raise ShardError(f"malformed manifest: {e}") from None
 
 

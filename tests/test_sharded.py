@@ -113,6 +113,31 @@ def test_header_step_disagreeing_with_manifest_is_refused(tmp_path):
         sharded.verify_sharded(tmp_path, 2, 100)
 
 
+@pytest.mark.parametrize("damage", ["truncated_json", "missing_key", "step_not_a_number",
+                                    "shards_not_a_list", "extra_shard_field"])
+def test_malformed_manifest_is_refused(tmp_path, damage):
+    w, m, v = _arrays(100)
+    man = _write_host_sharded(tmp_path, 5, w, m, v, 2)
+    text = json.dumps(man)
+    if damage == "truncated_json":
+        text = text[: len(text) // 2]
+    elif damage == "missing_key":
+        del man["world_size"]
+        text = json.dumps(man)
+    elif damage == "step_not_a_number":
+        man["step"] = "five"
+        text = json.dumps(man)
+    elif damage == "shards_not_a_list":
+        man["shards"] = 7
+        text = json.dumps(man)
+    else:
+        man["shards"][0]["owner"] = "someone"
+        text = json.dumps(man)
+    open(tmp_path / "manifest.json", "w").write(text)
+    with pytest.raises(sharded.ShardError, match="malformed"):
+        sharded.verify_sharded(tmp_path, 2, 100)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("world", [1, 3, 4, 8])
 def test_gpu_save_load_round_trip_matches_oracle_shards(tmp_path, world):
