@@ -486,7 +486,8 @@ def test_max_n_int32_limit_ragged_tail(dev):
     """n = 2^31 - 1, the largest n the int32 header can hold (n % 4 == 3, so
     the vector kernels end in a 3-element scalar tail): one update, norm
     against the oracle's streamed norm, w, m, v on the first, a middle and the
-    last 1 Mi elements."""
+    last 1 Mi elements; then the in-place clip of the same g (same norm, g * s
+    on those chunks) and grad_zero (the chunks and the last 3 elements)."""
     n = rcs.MAX_N
     wl = workloads.WORKLOADS["flat2e9"]
     chunk = 1 << 20
@@ -510,6 +511,19 @@ def test_max_n_int32_limit_ragged_tail(dev):
         oracle.adamw_elems(ow, og, om, ov, float(s), float(bc1), float(bc2), float(decay), wl.lr)
         _check_state(w[o:o + chunk], m[o:o + chunk], v[o:o + chunk], ow, om, ov,
                      f"max n chunk at {o}")
+    # the in-place clip and the buffer reset at the same size (g is still the
+    # gradient whose norm was just checked)
+    rcs.grad_clip_inplace(g, wl.clip)
+    assert _gpu_norm() == gpu_norm
+    for o in offs:
+        og = before[o][1].copy()
+        oracle.scale_grads(og, float(s))  # g * s in float32, s from the full-length norm
+        assert max_ulp(_host(g[o:o + chunk]), og) <= ULP_TOL, f"clip chunk at {o}"
+    rcs.grad_zero(g)
+    torch.cuda.synchronize()
+    for o in offs:
+        assert not bool(g[o:o + chunk].any()), f"grad_zero chunk at {o}"
+    assert not bool(g[-3:].any())
 
 
 @pytest.mark.parametrize("case", ["clip_inf", "lr_zero", "wd_zero", "t_max", "zero_grad",
