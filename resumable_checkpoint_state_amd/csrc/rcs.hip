@@ -347,8 +347,11 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 // per-wave float64 square root and division cost more than the launch (one
 // wave per block: 529.7 against 552.2 us for the update at the ANDREA-120M
 // size, measured in one process).
-template <bool FOLD>
-__device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *__restrict__ g,
+// GVEC = true: g's body is 16-byte aligned like w's and is read as one vector
+// per lane; false: g lies at another 16-byte phase (w, m and v share theirs)
+// and each lane reads its four elements of g with 4-byte streaming loads.
+template <bool FOLD, bool GVEC>
+__device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *__restrict__ gf,
                                             f32x4 *__restrict__ m, f32x4 *__restrict__ v,
                                             int64_t n, int head,
                                             const double *__restrict__ partials, int nparts,
@@ -365,7 +368,13 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *
     double xp[kPartsPerLane];
     if constexpr (FOLD) load_partials(partials, nparts, xp);
     const int64_t ic = i < n4 ? i : n4 - 1;
-    f32x4 gr = ld_stream(g + ic);
+    f32x4 gr;
+    if constexpr (GVEC) {
+        gr = ld_stream(reinterpret_cast<const f32x4 *>(gf) + ic);
+    } else {
+        const float *p = gf + 4 * ic;
+        gr = f32x4{ld_stream(p), ld_stream(p + 1), ld_stream(p + 2), ld_stream(p + 3)};
+    }
     f32x4 wr = ld_stream(w + ic);
     f32x4 mr = ld_stream(m + ic);
     f32x4 vr = ld_stream(v + ic);
@@ -389,7 +398,6 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *
     float *wf = reinterpret_cast<float *>(w);
     float *mf = reinterpret_cast<float *>(m);
     float *vf = reinterpret_cast<float *>(v);
-    const float *gf = reinterpret_cast<const float *>(g);
     if (blockIdx.x == 0 && (int)threadIdx.x < head) {
         const int64_t k = (int64_t)threadIdx.x - head;
         float ww = wf[k], mm = mf[k], vv = vf[k];
@@ -411,20 +419,39 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const f32x4 *
 // a3 after grad_norm_final. w, g, m, v point `head` (0-63) elements past the
 // arrays' starts, at 16-byte boundaries; n counts from there.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
-    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
     f32x4 *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false>(w, g, m, v, n, head, nullptr, 0, 0.0f, const_cast<ClipScalars *>(sc), h,
-                       nullptr);
+    update_body<false, true>(w, g, m, v, n, head, nullptr, 0, 0.0f,
+                             const_cast<ClipScalars *>(sc), h, nullptr);
 }
 
 // a2 + a3 in one kernel (small n).
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
-    f32x4 *__restrict__ w, const f32x4 *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
     f32x4 *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
     float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
+    update_body<true, true>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
+}
+
+// The same two kernels for a g at another 16-byte phase than w, m and v
+// (e.g. the state carved from one flat buffer, the gradient from another):
+// w, m, v keep their 16-byte vectors, g is read four floats per lane.
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_gs(
+    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
+    StepScalars h) {
+    update_body<false, false>(w, g, m, v, n, head, nullptr, 0, 0.0f,
+                              const_cast<ClipScalars *>(sc), h, nullptr);
+}
+
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_gs_fold(
+    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
+    f32x4 *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
+    float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
+    __shared__ double lds[kUpdThreads / kWave];
+    update_body<true, false>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
 }
 
 // a3 for arrays that are not all 16-byte aligned: same arithmetic per element.
@@ -732,13 +759,13 @@ int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
-// The head for w, g, m and v: w's (its body then starts on a 256-byte
-// boundary), provided the four lie equally far from a 16-byte boundary, so
-// that all four bodies are 16-byte aligned; -1 otherwise.
-int common_head(const void *w, const void *g, const void *m, const void *v, int64_t n) {
+// The head for the state arrays: w's (its body then starts on a 256-byte
+// boundary), provided w, m and v lie equally far from a 16-byte boundary, so
+// that all three bodies are 16-byte aligned; -1 otherwise.
+int state_head(const void *w, const void *m, const void *v, int64_t n) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(w) & 15u;
     const auto same = [a](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == a; };
-    return (same(g) && same(m) && same(v)) ? head_of(w, n) : -1;
+    return (same(m) && same(v)) ? head_of(w, n) : -1;
 }
 
 // Whether the vector kernels do the final reduction themselves (two launches)
@@ -746,8 +773,9 @@ int common_head(const void *w, const void *g, const void *m, const void *v, int6
 // costs more than the reduction at the head of every wave.
 bool fold_final(int64_t n) { return n <= (int64_t)RCS_FOLD_MAX_N; }
 
-// The whole step a1..a3. Vector form (w, g, m, v equally far from a 16-byte
-// boundary, at least 4 elements past the head): the partial kernel,
+// The whole step a1..a3. Vector form (w, m, v equally far from a 16-byte
+// boundary, at least 4 elements past the head; g at the same phase, or at
+// another with its own vectors read as floats): the partial kernel,
 // [grad_norm_final,] the update kernel on the aligned body, which also takes
 // the head elements. Otherwise: partial, final, scalar update.
 // ev (optional, profiling): ev[0] / ev[1] take the start of the partial kernel
@@ -755,26 +783,29 @@ bool fold_final(int64_t n) { return n <= (int64_t)RCS_FOLD_MAX_N; }
 int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float clip,
                 const StepScalars &h, Workspace *ws, hipStream_t stream, hipEvent_t *ev) {
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-    const int head = common_head(w, g, m, v, n);
-    if (head >= 0) {
+    const int head = state_head(w, m, v, n);
+    const uintptr_t wa = reinterpret_cast<uintptr_t>(w), ga = reinterpret_cast<uintptr_t>(g);
+    const bool gvec = (ga & 15u) == (wa & 15u);
+    if (head >= 0 && (gvec || (ga & 3u) == 0)) {
         const int64_t nb = n - head;  // elements from the 16-byte boundary on
         const int64_t blocks = ((nb >> 2) + kUpdThreads - 1) / kUpdThreads;
         f32x4 *w4 = reinterpret_cast<f32x4 *>(w + head), *m4 = reinterpret_cast<f32x4 *>(m + head);
         f32x4 *v4 = reinterpret_cast<f32x4 *>(v + head);
-        const f32x4 *g4 = reinterpret_cast<const f32x4 *>(g + head);
+        const float *gb = g + head;
         if (fold_final(n)) {
             launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr,
                            ev ? ev[1] : nullptr);
-            hipExtLaunchKernelGGL(adamw_update_vec_fold, dim3((unsigned)blocks),
-                                  dim3(kUpdThreads), 0, stream, e2, e3, 0, w4, g4, m4, v4, nb,
-                                  head, (const double *)ws->partials, norm_blocks(n), clip,
-                                  ws->scalars, h);
+            hipExtLaunchKernelGGL(gvec ? adamw_update_vec_fold : adamw_update_vec_gs_fold,
+                                  dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream, e2, e3,
+                                  0, w4, gb, m4, v4, nb, head, (const double *)ws->partials,
+                                  norm_blocks(n), clip, ws->scalars, h);
         } else {
             const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
             if (rc != RCS_OK) return rc;
-            hipExtLaunchKernelGGL(adamw_update_vec, dim3((unsigned)blocks), dim3(kUpdThreads),
-                                  0, stream, e2, e3, 0, w4, g4, m4, v4, nb, head,
-                                  (const ClipScalars *)ws->scalars, h);
+            hipExtLaunchKernelGGL(gvec ? adamw_update_vec : adamw_update_vec_gs,
+                                  dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream, e2, e3,
+                                  0, w4, gb, m4, v4, nb, head, (const ClipScalars *)ws->scalars,
+                                  h);
         }
     } else {
         const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);

@@ -174,14 +174,17 @@ def test_update_parity_ragged_sizes(dev, n):
 # 256-byte boundary (64 - offset elements: bodies of exactly 4 and 7 behind a
 # 63-element head, head and tail in one block), or to the next 16-byte one when
 # fewer than 4 elements would follow (heads of 1-3, bodies of 4, 5 and 7); g, m
-# and v may sit at other 256-byte phases (1, 5, 9, 65). Both final-reduction
-# forms. Offsets unequal modulo 4, and views too short for either head, take
-# the scalar kernels.
+# and v may sit at other 256-byte phases (1, 5, 9, 65). When only g's offset
+# differs modulo 4, the vector kernels read g four floats per lane (the _gs
+# kernels). Both final-reduction forms. w, m, v at different offsets modulo
+# 4, and views too short for either head, take the scalar kernels.
 UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3), 50_001),
                    ((1, 1, 1, 1), 67), ((1, 1, 1, 1), 70), ((2, 2, 2, 2), 66),
                    ((3, 3, 3, 3), 5), ((3, 3, 3, 3), 6), ((1, 1, 1, 1), 7), ((2, 2, 2, 2), 9),
                    ((1, 5, 9, 65), 50_001), ((4, 8, 12, 0), 4099),
                    ((1, 1, 1, 1), 8_388_611), ((3, 3, 3, 3), 8_388_608),
+                   ((1, 2, 1, 1), 50_001), ((0, 3, 0, 0), 12_800_003), ((2, 0, 2, 2), 67),
+                   ((3, 1, 3, 3), 8_388_611), ((1, 0, 1, 1), 8_388_608),
                    ((1, 2, 0, 3), 50_001), ((0, 0, 0, 1), 4099), ((2, 2, 2, 2), 5)]
 
 
@@ -265,11 +268,11 @@ def test_step_norm_same_bits_as_final_kernel(dev, n):
 
 
 @pytest.mark.parametrize("n,off,goff", [(10_000, 0, 0), (5_000_001, 0, 0), (10_000, 1, 1),
-                                         (10_000, 1, 2), (3, 0, 0)])
+                                         (10_000, 1, 2), (9_000_001, 0, 3), (3, 0, 0)])
 def test_nonfinite_norm_skips_update(dev, n, off, goff):
     """Every update form skips: the vector kernels (equal offsets, with and
-    without a peeled head, both final-reduction forms) and the scalar one after
-    the final kernel (unequal offsets, n < 4)."""
+    without a peeled head, both final-reduction forms; g at another phase than
+    w, m, v) and the scalar one after the final kernel (n < 4)."""
     w = workloads.custom(104, n + off, 0.02, device=dev)[off:]
     m = workloads.custom(105, n + off, 0.01, device=dev)[off:]
     v = workloads.custom(106, n + off, 0.01, device=dev)[off:].abs_()
