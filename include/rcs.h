@@ -89,15 +89,15 @@ int rcs_init(int device, hipStream_t stream);
  * left untouched); read the norm with last_grad_norm.
  * The reduction order depends only on n and on g's address modulo 256
  * bytes, so results are deterministic for a given buffer.
- * When w, m and v lie equally far (0, 4, 8 or 12 bytes) from a 16-byte
- * boundary, the update kernel streams 16-byte vectors from w's next 256-byte
+ * The update kernel streams w in 16-byte vectors from its next 256-byte
  * boundary on and takes the 0-63 elements before it separately (with fewer
- * than 4 elements after that boundary: from the next 16-byte one); g is read
- * the same way when it shares that phase, else four floats per lane. Up to
- * n = 8,388,608 the update kernel also does the final reduction itself, in
- * grad_norm_final's order (two launches instead of three; the same norm bits
- * as grad_global_norm). Other arrays take partial, final and a scalar update
- * kernel with the same arithmetic.
+ * than 4 elements after that boundary: from the next 16-byte one); each of g,
+ * m and v lying equally far from a 16-byte boundary as w is accessed the same
+ * way, the others four floats per lane. Up to n = 8,388,608 the update kernel
+ * also does the final reduction itself, in grad_norm_final's order (two
+ * launches instead of three; the same norm bits as grad_global_norm). Arrays
+ * too short for a head and one vector take partial, final and a scalar
+ * update kernel with the same arithmetic.
  */
 int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                     float lr, float wd, float clip, hipStream_t stream);

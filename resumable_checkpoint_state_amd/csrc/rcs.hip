@@ -38,11 +38,11 @@
 //   * adamw_update_vec_fold: for n up to 8,388,608, where the step is bound
 //     by launch cost, every wave does grad_norm_final's reduction itself (the
 //     same bits) and the step is two launches instead of three.
-//   * Arrays that start off a 16-byte boundary, all four by the same amount
-//     (views into a flat buffer), keep the vector kernels: block 0 takes the
-//     0-63 elements before w's next 256-byte boundary one per lane, and the
-//     waves stream whole cache lines from there. Arrays at different 16-byte
-//     phases take scalar kernels with the same arithmetic.
+//   * Arrays that start off a 16-byte boundary (views into a flat buffer)
+//     keep the vector kernels: block 0 takes the 0-63 elements before w's
+//     next 256-byte boundary one per lane, and the waves stream whole cache
+//     lines from there; g, m or v at another 16-byte phase than w take four
+//     4-byte accesses per lane (adamw_update_mixed).
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -334,6 +334,26 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 #endif
 }
 
+// Four consecutive floats of a lane: one 16-byte access when the array shares
+// w's 16-byte phase (VEC), else four 4-byte accesses (still streaming).
+template <bool VEC>
+__device__ __forceinline__ f32x4 ld4(const float *p) {
+    if constexpr (VEC) return ld_stream(reinterpret_cast<const f32x4 *>(p));
+    else return f32x4{ld_stream(p), ld_stream(p + 1), ld_stream(p + 2), ld_stream(p + 3)};
+}
+
+template <bool VEC>
+__device__ __forceinline__ void st4(float *p, f32x4 x) {
+    if constexpr (VEC) {
+        st_stream(reinterpret_cast<f32x4 *>(p), x);
+    } else {
+        st_stream(p, x.x);
+        st_stream(p + 1, x.y);
+        st_stream(p + 2, x.z);
+        st_stream(p + 3, x.w);
+    }
+}
+
 // a3: clip factor and AdamW on one 16-byte vector of w, g, m, v per lane, with
 // streaming loads and stores; block b works in contiguous region b % 8 (one
 // region per XCD). Every load is unconditional (lanes past the end re-read the
@@ -347,12 +367,12 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 // per-wave float64 square root and division cost more than the launch (one
 // wave per block: 529.7 against 552.2 us for the update at the ANDREA-120M
 // size, measured in one process).
-// GVEC = true: g's body is 16-byte aligned like w's and is read as one vector
-// per lane; false: g lies at another 16-byte phase (w, m and v share theirs)
-// and each lane reads its four elements of g with 4-byte streaming loads.
-template <bool FOLD, bool GVEC>
+// w's body is 16-byte aligned (the head is w's); GV, MV, VV say whether g, m
+// and v share w's 16-byte phase and so take one 16-byte access per lane, or
+// lie at another and take four 4-byte accesses (ld4 / st4).
+template <bool FOLD, bool GV, bool MV, bool VV>
 __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *__restrict__ gf,
-                                            f32x4 *__restrict__ m, f32x4 *__restrict__ v,
+                                            float *__restrict__ mf, float *__restrict__ vf,
                                             int64_t n, int head,
                                             const double *__restrict__ partials, int nparts,
                                             float clip, ClipScalars *__restrict__ sc,
@@ -368,16 +388,10 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *
     double xp[kPartsPerLane];
     if constexpr (FOLD) load_partials(partials, nparts, xp);
     const int64_t ic = i < n4 ? i : n4 - 1;
-    f32x4 gr;
-    if constexpr (GVEC) {
-        gr = ld_stream(reinterpret_cast<const f32x4 *>(gf) + ic);
-    } else {
-        const float *p = gf + 4 * ic;
-        gr = f32x4{ld_stream(p), ld_stream(p + 1), ld_stream(p + 2), ld_stream(p + 3)};
-    }
+    f32x4 gr = ld4<GV>(gf + 4 * ic);
     f32x4 wr = ld_stream(w + ic);
-    f32x4 mr = ld_stream(m + ic);
-    f32x4 vr = ld_stream(v + ic);
+    f32x4 mr = ld4<MV>(mf + 4 * ic);
+    f32x4 vr = ld4<VV>(vf + 4 * ic);
     ClipScalars cs;
     if constexpr (FOLD) {
         cs = final_reduce(xp, nparts, clip, lds);
@@ -390,14 +404,12 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *
     if (i < n4) {
         adamw_vec4(wr, gr, mr, vr, s, h);
         st_stream(w + i, wr);
-        st_stream(m + i, mr);
-        st_stream(v + i, vr);
+        st4<MV>(mf + 4 * i, mr);
+        st4<VV>(vf + 4 * i, vr);
     }
     // block 0: the head elements before the body (indices -head .. -1);
     // the last block: the n % 4 after the last vector
     float *wf = reinterpret_cast<float *>(w);
-    float *mf = reinterpret_cast<float *>(m);
-    float *vf = reinterpret_cast<float *>(v);
     if (blockIdx.x == 0 && (int)threadIdx.x < head) {
         const int64_t k = (int64_t)threadIdx.x - head;
         float ww = wf[k], mm = mf[k], vv = vf[k];
@@ -419,42 +431,47 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *
 // a3 after grad_norm_final. w, g, m, v point `head` (0-63) elements past the
 // arrays' starts, at 16-byte boundaries; n counts from there.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
-    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
+    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false, true>(w, g, m, v, n, head, nullptr, 0, 0.0f,
-                             const_cast<ClipScalars *>(sc), h, nullptr);
+    update_body<false, true, true, true>(w, g, m, v, n, head, nullptr, 0, 0.0f,
+                                         const_cast<ClipScalars *>(sc), h, nullptr);
 }
 
 // a2 + a3 in one kernel (small n).
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
-    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
+    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
     float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true, true>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
+    update_body<true, true, true, true>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h,
+                                        lds);
 }
 
-// The same two kernels for a g at another 16-byte phase than w, m and v
-// (e.g. the state carved from one flat buffer, the gradient from another):
-// w, m, v keep their 16-byte vectors, g is read four floats per lane.
-__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_gs(
-    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
+// The same two kernels when some of g, m, v lie at another 16-byte phase than
+// w (e.g. w a view into a flat parameter buffer at an odd offset, m and v
+// fresh allocations): w and the arrays at its phase keep 16-byte vectors, the
+// others take four 4-byte accesses per lane.
+template <bool GV, bool MV, bool VV>
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_mixed(
+    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false, false>(w, g, m, v, n, head, nullptr, 0, 0.0f,
-                              const_cast<ClipScalars *>(sc), h, nullptr);
+    update_body<false, GV, MV, VV>(w, g, m, v, n, head, nullptr, 0, 0.0f,
+                                   const_cast<ClipScalars *>(sc), h, nullptr);
 }
 
-__global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_gs_fold(
-    f32x4 *__restrict__ w, const float *__restrict__ g, f32x4 *__restrict__ m,
-    f32x4 *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
+template <bool GV, bool MV, bool VV>
+__global__ __launch_bounds__(kUpdThreads) void adamw_update_mixed_fold(
+    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
     float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true, false>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
+    update_body<true, GV, MV, VV>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
 }
 
-// a3 for arrays that are not all 16-byte aligned: same arithmetic per element.
+// a3 for arrays that are not 4-byte aligned or too short for a head and one
+// vector: same arithmetic per element.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_scalar(
     float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
     float *__restrict__ v, int64_t n, const ClipScalars *__restrict__ sc, StepScalars h) {
@@ -759,53 +776,103 @@ int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
-// The head for the state arrays: w's (its body then starts on a 256-byte
-// boundary), provided w, m and v lie equally far from a 16-byte boundary, so
-// that all three bodies are 16-byte aligned; -1 otherwise.
-int state_head(const void *w, const void *m, const void *v, int64_t n) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(w) & 15u;
-    const auto same = [a](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == a; };
-    return (same(m) && same(v)) ? head_of(w, n) : -1;
-}
-
 // Whether the vector kernels do the final reduction themselves (two launches)
 // rather than after grad_norm_final (three): only while the launch it saves
 // costs more than the reduction at the head of every wave.
 bool fold_final(int64_t n) { return n <= (int64_t)RCS_FOLD_MAX_N; }
 
-// The whole step a1..a3. Vector form (w, m, v equally far from a 16-byte
-// boundary, at least 4 elements past the head; g at the same phase, or at
-// another with its own vectors read as floats): the partial kernel,
-// [grad_norm_final,] the update kernel on the aligned body, which also takes
-// the head elements. Otherwise: partial, final, scalar update.
+// Arguments of the update kernels after the norm kernels.
+struct UpdateLaunch {
+    dim3 grid;
+    f32x4 *w;
+    const float *g;
+    float *m, *v;
+    int64_t nb;
+    int head;
+    bool fold;
+    const double *partials;
+    int nparts;
+    float clip;
+    ClipScalars *sc;
+    StepScalars h;
+    hipStream_t stream;
+    hipEvent_t e2, e3;
+};
+
+template <bool GV, bool MV, bool VV>
+void launch_update(const UpdateLaunch &a) {
+    const dim3 block(kUpdThreads);
+    if constexpr (GV && MV && VV) {
+        if (a.fold)
+            hipExtLaunchKernelGGL(adamw_update_vec_fold, a.grid, block, 0, a.stream, a.e2, a.e3, 0,
+                                  a.w, a.g, a.m, a.v, a.nb, a.head, a.partials, a.nparts, a.clip,
+                                  a.sc, a.h);
+        else
+            hipExtLaunchKernelGGL(adamw_update_vec, a.grid, block, 0, a.stream, a.e2, a.e3, 0, a.w,
+                                  a.g, a.m, a.v, a.nb, a.head, (const ClipScalars *)a.sc, a.h);
+    } else {
+        if (a.fold)
+            hipExtLaunchKernelGGL(adamw_update_mixed_fold<GV, MV, VV>, a.grid, block, 0, a.stream,
+                                  a.e2, a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head, a.partials,
+                                  a.nparts, a.clip, a.sc, a.h);
+        else
+            hipExtLaunchKernelGGL(adamw_update_mixed<GV, MV, VV>, a.grid, block, 0, a.stream, a.e2,
+                                  a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head,
+                                  (const ClipScalars *)a.sc, a.h);
+    }
+}
+
+// The whole step a1..a3. Vector form (all four arrays 4-byte aligned, at
+// least 4 elements past w's head): the partial kernel, [grad_norm_final,] the
+// update kernel on w's aligned body, which also takes the head elements; g, m
+// and v at w's 16-byte phase are accessed as 16-byte vectors, the others four
+// floats per lane. Otherwise: partial, final, scalar update.
 // ev (optional, profiling): ev[0] / ev[1] take the start of the partial kernel
 // and the end of the last norm kernel, ev[2] / ev[3] the update's start / end.
 int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float clip,
                 const StepScalars &h, Workspace *ws, hipStream_t stream, hipEvent_t *ev) {
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-    const int head = state_head(w, m, v, n);
     const uintptr_t wa = reinterpret_cast<uintptr_t>(w), ga = reinterpret_cast<uintptr_t>(g);
-    const bool gvec = (ga & 15u) == (wa & 15u);
-    if (head >= 0 && (gvec || (ga & 3u) == 0)) {
-        const int64_t nb = n - head;  // elements from the 16-byte boundary on
-        const int64_t blocks = ((nb >> 2) + kUpdThreads - 1) / kUpdThreads;
-        f32x4 *w4 = reinterpret_cast<f32x4 *>(w + head), *m4 = reinterpret_cast<f32x4 *>(m + head);
-        f32x4 *v4 = reinterpret_cast<f32x4 *>(v + head);
-        const float *gb = g + head;
-        if (fold_final(n)) {
+    const uintptr_t ma = reinterpret_cast<uintptr_t>(m), va = reinterpret_cast<uintptr_t>(v);
+    const int head = ((ga | ma | va) & 3u) == 0 ? head_of(w, n) : -1;
+    if (head >= 0) {
+        const bool fold = fold_final(n);
+        if (fold) {
             launch_partial(g, n, h.gscale, ws, stream, ev ? ev[0] : nullptr,
                            ev ? ev[1] : nullptr);
-            hipExtLaunchKernelGGL(gvec ? adamw_update_vec_fold : adamw_update_vec_gs_fold,
-                                  dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream, e2, e3,
-                                  0, w4, gb, m4, v4, nb, head, (const double *)ws->partials,
-                                  norm_blocks(n), clip, ws->scalars, h);
         } else {
             const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
             if (rc != RCS_OK) return rc;
-            hipExtLaunchKernelGGL(gvec ? adamw_update_vec : adamw_update_vec_gs,
-                                  dim3((unsigned)blocks), dim3(kUpdThreads), 0, stream, e2, e3,
-                                  0, w4, gb, m4, v4, nb, head, (const ClipScalars *)ws->scalars,
-                                  h);
+        }
+        UpdateLaunch a;
+        a.nb = n - head;  // elements from w's boundary on
+        a.grid = dim3((unsigned)(((a.nb >> 2) + kUpdThreads - 1) / kUpdThreads));
+        a.w = reinterpret_cast<f32x4 *>(w + head);
+        a.g = g + head;
+        a.m = m + head;
+        a.v = v + head;
+        a.head = head;
+        a.fold = fold;
+        a.partials = ws->partials;
+        a.nparts = norm_blocks(n);
+        a.clip = clip;
+        a.sc = ws->scalars;
+        a.h = h;
+        a.stream = stream;
+        a.e2 = e2;
+        a.e3 = e3;
+        const uintptr_t ph = wa & 15u;
+        const int mask = ((ga & 15u) == ph ? 4 : 0) | ((ma & 15u) == ph ? 2 : 0) |
+                         ((va & 15u) == ph ? 1 : 0);
+        switch (mask) {
+            case 7: launch_update<true, true, true>(a); break;
+            case 6: launch_update<true, true, false>(a); break;
+            case 5: launch_update<true, false, true>(a); break;
+            case 4: launch_update<true, false, false>(a); break;
+            case 3: launch_update<false, true, true>(a); break;
+            case 2: launch_update<false, true, false>(a); break;
+            case 1: launch_update<false, false, true>(a); break;
+            default: launch_update<false, false, false>(a); break;
         }
     } else {
         const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);

@@ -174,10 +174,12 @@ def test_update_parity_ragged_sizes(dev, n):
 # 256-byte boundary (64 - offset elements: bodies of exactly 4 and 7 behind a
 # 63-element head, head and tail in one block), or to the next 16-byte one when
 # fewer than 4 elements would follow (heads of 1-3, bodies of 4, 5 and 7); g, m
-# and v may sit at other 256-byte phases (1, 5, 9, 65). When only g's offset
-# differs modulo 4, the vector kernels read g four floats per lane (the _gs
-# kernels). Both final-reduction forms. w, m, v at different offsets modulo
-# 4, and views too short for either head, take the scalar kernels.
+# and v may sit at other 256-byte phases (1, 5, 9, 65). Arrays among g, m, v
+# whose offset differs from w's modulo 4 take four 4-byte accesses per lane
+# in the vector kernels (adamw_update_mixed: each of the seven combinations of
+# which arrays differ appears here). Both
+# final-reduction forms. Views too short for either head take the scalar
+# kernels.
 UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3), 50_001),
                    ((1, 1, 1, 1), 67), ((1, 1, 1, 1), 70), ((2, 2, 2, 2), 66),
                    ((3, 3, 3, 3), 5), ((3, 3, 3, 3), 6), ((1, 1, 1, 1), 7), ((2, 2, 2, 2), 9),
@@ -185,7 +187,10 @@ UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3)
                    ((1, 1, 1, 1), 8_388_611), ((3, 3, 3, 3), 8_388_608),
                    ((1, 2, 1, 1), 50_001), ((0, 3, 0, 0), 12_800_003), ((2, 0, 2, 2), 67),
                    ((3, 1, 3, 3), 8_388_611), ((1, 0, 1, 1), 8_388_608),
-                   ((1, 2, 0, 3), 50_001), ((0, 0, 0, 1), 4099), ((2, 2, 2, 2), 5)]
+                   ((1, 2, 0, 3), 50_001), ((0, 0, 0, 1), 4099), ((1, 0, 0, 0), 50_001),
+                   ((0, 1, 2, 3), 8_388_608), ((3, 3, 0, 3), 12_800_003), ((2, 2, 2, 0), 66),
+                   ((1, 1, 2, 1), 70), ((1, 1, 0, 2), 50_001), ((1, 0, 1, 2), 4099),
+                   ((3, 0, 1, 3), 12_800_003), ((2, 2, 2, 2), 5)]
 
 
 @pytest.mark.parametrize("offs,n", UNALIGNED_CASES)
