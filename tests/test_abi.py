@@ -171,3 +171,45 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_unpack_header_decisions_match_the_oracle_on_random_buffers(L):
+    """2,000 seeded random step-file images (steps and sizes around the
+    edges: negative, zero, the expected n and its neighbours, int32 extremes;
+    lengths exact, one byte off, short of the header) through the library's
+    and the oracle's unpack: the same status for every rejected image (the
+    library's checks run before any device pointer is looked at, and leave
+    the step output untouched), and for every image the oracle accepts the
+    library passes the header checks too (it then refuses the stand-in device
+    pointers with RCS_EINVAL, having copied nothing)."""
+    import numpy as np
+    import oracle
+
+    rng = np.random.default_rng(20240611)
+    steps = [-(2**31), -5, -1, 0, 1, 7, 112_700, 2**31 - 1]
+    seen = {oracle.OK: 0, oracle.ESIZE: 0, oracle.EHEADER: 0}
+    for case in range(2000):
+        n_exp = int(rng.integers(1, 65))
+        step = int(rng.choice(steps))
+        n_hdr = int(rng.choice([n_exp, n_exp, n_exp - 1, n_exp + 1, 0, -n_exp, 2**31 - 1,
+                                -(2**31), int(rng.integers(1, 200))]))
+        body = 12 * n_hdr if 0 < n_hdr <= 64 else 12 * n_exp
+        length = int(rng.choice([8 + body, 8 + body, 8 + body - 1, 8 + body + 1,
+                                 int(rng.integers(0, 8)), 8 + 12 * n_exp]))
+        full = struct.pack("<ii", step, n_hdr) + rng.integers(0, 256, body + 16,
+                                                             dtype=np.uint8).tobytes()
+        b = bytearray(full[:length]) if length > 0 else bytearray(1)
+        w, m, v = (np.zeros(n_exp, np.float32) for _ in range(3))
+        orc, _ = oracle.ckpt_unpack(np.frombuffer(bytes(b[:length]), np.uint8).copy()
+                                    if length > 0 else np.zeros(0, np.uint8), w, m, v)
+        arr = (ctypes.c_uint8 * len(b)).from_buffer(b)
+        out = ctypes.c_int32(-7)
+        rc = L.ckpt_unpack(arr, length, n_exp, ctypes.byref(out), FAKE, FAKE, FAKE, None)
+        ctx = (case, step, n_hdr, n_exp, length)
+        if orc == oracle.OK:
+            assert rc == rcs.EINVAL, ctx
+        else:
+            assert rc == orc, ctx
+        assert out.value == -7, ctx
+        seen[orc] += 1
+    assert min(seen.values()) > 100, seen
