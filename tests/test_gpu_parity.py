@@ -377,6 +377,35 @@ def test_resume_bit_identical_flat262k(dev):
     _check_state(w, m, v, ow, om, ov, "flat262k after 80 steps")
 
 
+@pytest.mark.parametrize("lost", ["moments", "step_count"])
+def test_resume_without_the_full_state_differs(dev, lost):
+    """The negative half of the resume lesson's test, on the GPU: resuming
+    flat262k at step 40 from the weights alone (m = v = 0) or with the update
+    counter restarted at 1 (bias corrections of a fresh run) leaves a final w
+    measurably off the straight run's, so the test above would notice a pack
+    that dropped either."""
+    wl = workloads.WORKLOADS["flat262k"]
+    n, steps, pack_at = wl.n, wl.steps, 40
+    w0 = workloads.init_params(wl, device=dev)
+    g = torch.empty(n, device=dev)
+    w, (m, v) = w0.clone(), workloads.zeros_like_state(n, device=dev)
+    for t in range(1, pack_at + 1):
+        workloads.grads(wl, t, device=dev, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+    w2, m2, v2 = w.clone(), m.clone(), v.clone()
+    if lost == "moments":
+        m2.zero_()
+        v2.zero_()
+    for t in range(pack_at + 1, steps + 1):
+        workloads.grads(wl, t, device=dev, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        t2 = t if lost == "moments" else t - pack_at
+        rcs.adamw_clip_step(w2, g, m2, v2, t2, wl.lr, wl.wd, wl.clip)
+    torch.cuda.synchronize()
+    diff = float((w - w2).abs().max())
+    assert diff > 1e-4, (lost, diff)
+
+
 def test_resume_bit_identical_andrea12m(dev):
     wl = workloads.WORKLOADS["andrea12m"]
     _straight_vs_resumed(dev, wl, 20, 10)
