@@ -248,6 +248,47 @@ def test_signal_driven_step_files_resume_bit_identical(dev, tmp_path, mode):
     assert buf.numpy().tobytes() == final
 
 
+def test_resume_after_sigkill_redoes_the_lost_updates(dev, tmp_path):
+    """A crash between checkpoints: the child writes a step file every 25
+    updates, finishes update 60 and is killed with SIGKILL (while it waits on
+    the host, no device work or write in flight). A second child resumes from
+    the newest valid file (step 50), redoes 51-60 and runs to 100; its final
+    file is byte-identical to a straight run's."""
+    wl, n, total = "flat262k", 262_144, 100
+    cmd = [sys.executable, "-u", os.path.join(HERE, "resume_child.py"), str(tmp_path), wl,
+           str(n), str(total), "0", "0", "sync", "25"]
+    p = subprocess.Popen(cmd + ["60"], stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                         text=True)
+    stalled = False
+    try:
+        for line in p.stdout:
+            print(line, end="")
+            if "stalled after step 60" in line:
+                stalled = True
+                break
+    finally:
+        p.kill()
+        p.wait(timeout=60)
+    assert stalled, p.stderr.read()[-2000:]
+    assert p.returncode == -9
+    assert sorted(os.listdir(tmp_path)) == ["step_000025.bin", "step_000050.bin"]
+    r2 = subprocess.run(cmd + ["0"], capture_output=True, text=True, timeout=240)
+    print(r2.stdout, r2.stderr[-2000:])
+    assert r2.returncode == 0 and "resumed at step 50" in r2.stdout
+    final = open(tmp_path / "step_000100.bin", "rb").read()
+    W = workloads.WORKLOADS[wl]
+    w = workloads.init_params(W, device=dev, n=n)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    g = torch.empty(n, device=dev)
+    for t in range(1, total + 1):
+        workloads.grads(W, t, device=dev, n=n, out=g)
+        rcs.adamw_clip_step(w, g, m, v, t, W.lr, W.wd, W.clip)
+    buf = torch.empty(rcs.ckpt_bytes(n), dtype=torch.uint8, pin_memory=True)
+    rcs.ckpt_pack(total, w, m, v, buf)
+    torch.cuda.synchronize()
+    assert buf.numpy().tobytes() == final
+
+
 def test_weights_only_resume_diverges(dev):
     """Why m and v are in the file: resuming from the weights alone (m = v = 0,
     t restarted at 1) takes a different trajectory from the full resume,

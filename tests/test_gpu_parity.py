@@ -379,11 +379,11 @@ def test_resume_bit_identical_flat262k(dev):
 
 @pytest.mark.parametrize("lost", ["moments", "step_count"])
 def test_resume_without_the_full_state_differs(dev, lost):
-    """The negative half of the resume lesson's test, on the GPU: resuming
-    flat262k at step 40 from the weights alone (m = v = 0) or with the update
-    counter restarted at 1 (bias corrections of a fresh run) leaves a final w
-    measurably off the straight run's, so the test above would notice a pack
-    that dropped either."""
+    """Each piece of the state besides w on its own (test_gpu_next drops both
+    at once): resuming flat262k at step 40 without the moments (m = v = 0) or
+    with the update counter restarted at 1 (bias corrections of a fresh run)
+    leaves a final w measurably off the straight run's, so the resume tests
+    would notice a pack that dropped either."""
     wl = workloads.WORKLOADS["flat262k"]
     n, steps, pack_at = wl.n, wl.steps, 40
     w0 = workloads.init_params(wl, device=dev)
