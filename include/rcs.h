@@ -89,11 +89,14 @@ int rcs_init(int device, hipStream_t stream);
  * left untouched); read the norm with last_grad_norm.
  * The reduction order depends only on n and on g's address modulo 256
  * bytes, so results are deterministic for a given buffer.
- * The update kernel streams w in 16-byte vectors from its next 256-byte
- * boundary on and takes the 0-63 elements before it separately (with fewer
- * than 4 elements after that boundary: from the next 16-byte one); each of g,
- * m and v lying equally far from a 16-byte boundary as w is accessed the same
- * way, the others four floats per lane. Up to n = 8,388,608 the update kernel
+ * The update kernel streams the arrays in 16-byte vectors from the next
+ * 256-byte boundary of an anchor array on and takes the 0-63 elements before
+ * it separately (with fewer than 4 elements after that boundary: from the next
+ * 16-byte one). The anchor is w, or m when m and v lie at one 16-byte phase
+ * and w at another; arrays at the anchor's 16-byte phase take aligned
+ * vectors, the others aligned vectors shifted across neighbouring lanes
+ * (so every array is still read and written 16 bytes at a time). Up to
+ * n = 8,388,608 the update kernel
  * also does the final reduction itself, in grad_norm_final's order (two
  * launches instead of three; the same norm bits as grad_global_norm). Arrays
  * too short for a head and one vector take partial, final and a scalar
@@ -303,14 +306,6 @@ int rcs_ckpt_writer_destroy(rcs_ckpt_writer *writer);
  */
 int rcs_profile_enable(int on, int max_records, int every);
 int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *steps);
-
-/*
- * Self-test of the device arithmetic the update relies on: q[i] = a[i]/b[i]
- * and r[i] = sqrtf(a[i]) in float32 on the device, for comparison with the
- * host's IEEE results. Device float32 arrays of n elements.
- */
-int rcs_fp32_div_sqrt_probe(const float *a, const float *b, float *q, float *r, int64_t n,
-                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

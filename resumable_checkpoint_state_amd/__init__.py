@@ -20,7 +20,7 @@ from ._build import build
 
 __all__ = [
     "RcsError", "adamw_clip_step", "adamw_clip_step_accum", "grad_clip_inplace", "grad_zero", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
-    "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read", "fp32_div_sqrt_probe",
+    "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read",
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
     "ckpt_pack_async", "ckpt_pack_wait", "CkptWriter", "StepFileCheckpointer",
 ]
@@ -71,8 +71,6 @@ def lib() -> ctypes.CDLL:
     L.rcs_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     L.rcs_profile_read.restype = ctypes.c_int
-    L.rcs_fp32_div_sqrt_probe.argtypes = [f32p, f32p, f32p, f32p, i64, vp]
-    L.rcs_fp32_div_sqrt_probe.restype = ctypes.c_int
     L.adamw_clip_step_accum.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, f32, vp]
     L.adamw_clip_step_accum.restype = ctypes.c_int
     L.grad_clip_inplace.argtypes = [f32p, i64, f32, vp]
@@ -461,13 +459,3 @@ def profile_read():
     _check(lib().rcs_profile_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(k)),
            "rcs_profile_read")
     return a.value, b.value, k.value
-
-
-def fp32_div_sqrt_probe(a, b, stream=None):
-    n = a.numel()
-    q = torch.empty_like(a)
-    r = torch.empty_like(a)
-    _check(lib().rcs_fp32_div_sqrt_probe(_dev_f32(a, "a"), _dev_f32(b, "b", n), q.data_ptr(),
-                                         r.data_ptr(), n, _stream(stream)),
-           "rcs_fp32_div_sqrt_probe")
-    return q, r

@@ -10,6 +10,8 @@ SRC = os.path.join(PKG, "csrc", "rcs.hip")
 SRC_IO = os.path.join(PKG, "csrc", "ckpt_io.cpp")
 SRC_WRITER = os.path.join(PKG, "csrc", "ckpt_writer.cpp")
 LIB = os.path.join(PKG, "librcs.so")
+SRC_CEIL = os.path.join(PKG, "csrc", "ceilings.hip")
+LIB_CEIL = os.path.join(PKG, "libceilings.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 # -ffp-contract=off: every float op rounds on its own (no FMA contraction).
@@ -29,10 +31,11 @@ def hipcc() -> str:
     return p if os.path.exists(p) else "hipcc"
 
 
-def build(extra_flags: list[str] | None = None, out: str | None = None) -> str:
-    out = out or LIB
+def hipcc_shared(sources: list[str], out: str, extra_flags: list[str] | None = None) -> str:
+    """hipcc for gfx950 with the library's flags: sources -> shared object out
+    (written to a temporary name first, then renamed)."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", SRC, SRC_IO, SRC_WRITER, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", *sources, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag and says so
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
@@ -43,6 +46,15 @@ def build(extra_flags: list[str] | None = None, out: str | None = None) -> str:
         raise subprocess.CalledProcessError(r.returncode, cmd)
     os.replace(tmp, out)
     return out
+
+
+def build(extra_flags: list[str] | None = None, out: str | None = None) -> str:
+    return hipcc_shared([SRC, SRC_IO, SRC_WRITER], out or LIB, extra_flags)
+
+
+def build_ceilings() -> str:
+    """The streaming reference kernels bench.py times beside the update."""
+    return hipcc_shared([SRC_CEIL], LIB_CEIL)
 
 
 if __name__ == "__main__":

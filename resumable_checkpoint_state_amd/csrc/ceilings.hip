@@ -1,0 +1,105 @@
+// ceilings.hip -- streaming reference kernels that bench.py times beside the
+// update, to show how close the update's memory pattern runs to what the
+// chip's HBM gives that pattern. Not part of the library's C ABI and not on
+// the training path: they compute nothing of the method.
+//
+// All three use the update's launch shape (one wave per block, one 16-byte
+// vector of each array per lane, streaming loads and stores, block b working
+// in contiguous region b % 8 of the vectors), over float32 arrays of n4 16-byte
+// vectors:
+//   rcs_ceiling_read:  reads a; each block writes one float (sum of its lanes'
+//                      x components, so the loads are not dropped): 16 B/vector.
+//   rcs_ceiling_copy:  b = a: 32 B/vector.
+//   rcs_ceiling_4r3w:  reads w, g, m, v and writes w, m, v with one add per
+//                      element (w += g, m += g, v += g): the update's 28 B per
+//                      4 elements with trivial arithmetic.
+// Each returns 0 after a successful launch, -1 for bad arguments, -4 if the
+// launch failed. Pointers must be 16-byte aligned device memory holding n4
+// vectors (rcs_ceiling_read's `out`: one float per block, see
+// rcs_ceiling_blocks).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+constexpr int kLanes = 64;
+constexpr int64_t kRegions = 8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The update's block-to-chunk bijection: region b % 8, position b / 8.
+__device__ __forceinline__ int64_t chunk_of_block() {
+    const int64_t nblk = gridDim.x, c = blockIdx.x;
+    const int64_t q = nblk / kRegions, r = nblk % kRegions, x = c % kRegions, j = c / kRegions;
+    return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+__global__ __launch_bounds__(kLanes) void ceiling_read(const f32x4 *__restrict__ a, int64_t n4,
+                                                       float *__restrict__ out) {
+    const int64_t i = chunk_of_block() * kLanes + threadIdx.x;
+    float x = 0.0f;
+    if (i < n4) x = __builtin_nontemporal_load(a + i).x;
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kLanes);
+    if (threadIdx.x == 0) out[blockIdx.x] = x;
+}
+
+__global__ __launch_bounds__(kLanes) void ceiling_copy(const f32x4 *__restrict__ a,
+                                                       f32x4 *__restrict__ b, int64_t n4) {
+    const int64_t i = chunk_of_block() * kLanes + threadIdx.x;
+    if (i < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
+__global__ __launch_bounds__(kLanes) void ceiling_4r3w(f32x4 *__restrict__ w,
+                                                       const f32x4 *__restrict__ g,
+                                                       f32x4 *__restrict__ m,
+                                                       f32x4 *__restrict__ v, int64_t n4) {
+    const int64_t i = chunk_of_block() * kLanes + threadIdx.x;
+    if (i < n4) {
+        const f32x4 gg = __builtin_nontemporal_load(g + i);
+        const f32x4 ww = __builtin_nontemporal_load(w + i);
+        const f32x4 mm = __builtin_nontemporal_load(m + i);
+        const f32x4 vv = __builtin_nontemporal_load(v + i);
+        __builtin_nontemporal_store(ww + gg, w + i);
+        __builtin_nontemporal_store(mm + gg, m + i);
+        __builtin_nontemporal_store(vv + gg, v + i);
+    }
+}
+
+bool ok16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dim3 grid_of(int64_t n4) { return dim3((unsigned)((n4 + kLanes - 1) / kLanes)); }
+
+int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
+
+}  // namespace
+
+extern "C" {
+
+// Blocks (and so floats of rcs_ceiling_read's output) for n4 vectors.
+int64_t rcs_ceiling_blocks(int64_t n4) { return (n4 + kLanes - 1) / kLanes; }
+
+int rcs_ceiling_read(const float *a, int64_t n4, float *out, hipStream_t stream) {
+    if (!ok16(a) || out == nullptr || n4 < 1 || n4 > ((int64_t)1 << 36)) return -1;
+    hipLaunchKernelGGL(ceiling_read, grid_of(n4), dim3(kLanes), 0, stream,
+                       reinterpret_cast<const f32x4 *>(a), n4, out);
+    return launched();
+}
+
+int rcs_ceiling_copy(const float *a, float *b, int64_t n4, hipStream_t stream) {
+    if (!ok16(a) || !ok16(b) || n4 < 1 || n4 > ((int64_t)1 << 36)) return -1;
+    hipLaunchKernelGGL(ceiling_copy, grid_of(n4), dim3(kLanes), 0, stream,
+                       reinterpret_cast<const f32x4 *>(a), reinterpret_cast<f32x4 *>(b), n4);
+    return launched();
+}
+
+int rcs_ceiling_4r3w(float *w, const float *g, float *m, float *v, int64_t n4,
+                     hipStream_t stream) {
+    if (!ok16(w) || !ok16(g) || !ok16(m) || !ok16(v) || n4 < 1 || n4 > ((int64_t)1 << 36))
+        return -1;
+    hipLaunchKernelGGL(ceiling_4r3w, grid_of(n4), dim3(kLanes), 0, stream,
+                       reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
+                       reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n4);
+    return launched();
+}
+
+}  // extern "C"

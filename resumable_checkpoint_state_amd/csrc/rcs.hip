@@ -39,10 +39,12 @@
 //     by launch cost, every wave does grad_norm_final's reduction itself (the
 //     same bits) and the step is two launches instead of three.
 //   * Arrays that start off a 16-byte boundary (views into a flat buffer)
-//     keep the vector kernels: block 0 takes the 0-63 elements before w's
-//     next 256-byte boundary one per lane, and the waves stream whole cache
-//     lines from there; g, m or v at another 16-byte phase than w take four
-//     4-byte accesses per lane (adamw_update_mixed).
+//     keep the vector kernels: block 0 takes the 0-63 elements before the
+//     anchor array's next 256-byte boundary one per lane (the anchor is w, or
+//     m when m and v share a 16-byte phase that w does not), and the waves
+//     stream whole cache lines from there; an array at another 16-byte phase
+//     is still read and written in aligned 16-byte vectors, shifted by whole
+//     floats across neighbouring lanes (adamw_update_mixed).
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -66,37 +68,25 @@
 
 #pragma clang fp contract(off)
 
-// Launch-shape knobs (overridable at build time for sweeps).
-// Contiguous regions of the vectors the update streams at once: block b
-// works in region b % k. Blocks are dispatched round-robin over the chip's 8
-// XCDs, so with k = 8 each XCD streams its own contiguous eighth of w, g, m, v.
-// With one-wave blocks, over 14 buffer placements on one box the step took
-// 605.0-619.3 us (mean 611.0) with k = 8 against 612.9-631.1 (617.5) with
-// k = 4 (6 placements on another box: means 609.9 and 608.0; k = 2, 1, 16
-// and 32 were slower).
-#ifndef RCS_UPD_REGIONS
-#define RCS_UPD_REGIONS 8
-#endif
-#ifndef RCS_UPD_NT
-#define RCS_UPD_NT 1
-#endif
-// Largest n whose step folds the final norm reduction into the update kernel
-// (measured: folding saves 1.7-2.4 us per step up to 8,388,608 elements and
-// costs 4.8 us at 16,777,216 and 23 us at 124,356,864).
-#ifndef RCS_FOLD_MAX_N
-#define RCS_FOLD_MAX_N 8388608
-#endif
-// Bytes at the end of g that the norm pass reads with ordinary (cache-
-// allocating) loads so that the update, which reads g again right after,
-// finds them in the last-level cache; the rest is read with streaming loads.
-// A negative value reads all of g with ordinary loads.
-#ifndef RCS_NORM_CACHED_TAIL_BYTES
-#define RCS_NORM_CACHED_TAIL_BYTES (320LL << 20)
-#endif
-
 namespace {
 
 constexpr int kWave = 64;
+// Contiguous regions of the vectors the update streams at once: block b
+// works in region b % kRegions. Blocks are dispatched round-robin over the
+// chip's 8 XCDs, so with 8 regions each XCD streams its own contiguous eighth
+// of w, g, m, v. With one-wave blocks, over 14 buffer placements on one box
+// the step took 605.0-619.3 us (mean 611.0) with 8 regions against
+// 612.9-631.1 (617.5) with 4 (6 placements on another box: means 609.9 and
+// 608.0; 2, 1, 16 and 32 regions were slower).
+constexpr int64_t kRegions = 8;
+// Largest n whose step folds the final norm reduction into the update kernel
+// (measured: folding saves 1.7-2.4 us per step up to 8,388,608 elements and
+// costs 4.8 us at 16,777,216 and 23 us at 124,356,864).
+constexpr int64_t kFoldMaxN = 8388608;
+// Bytes at the end of g that the norm pass reads with ordinary (cache-
+// allocating) loads so that the update, which reads g again right after,
+// finds them in the last-level cache; the rest is read with streaming loads.
+constexpr int64_t kNormCachedTailBytes = 320LL << 20;
 // Norm pass: at most 256 blocks of 512 lanes, 4 loads of 16 B in flight per
 // lane (measured best of 256-1024 lanes x 2-8 loads with 256 blocks, and
 // faster per step than 2048 blocks x 256 lanes followed by a final kernel).
@@ -112,10 +102,7 @@ constexpr int kParts = kNormMaxBlocks;
 // i, i + L, i + 2L, ... in that order, so all three give the same bits.
 // One wave per block measured fastest: the update takes 529.7 us at the
 // ANDREA-120M size against 546.1 us with 256 lanes (same process).
-#ifndef RCS_UPD_THREADS
-#define RCS_UPD_THREADS 64
-#endif
-constexpr int kUpdThreads = RCS_UPD_THREADS;
+constexpr int kUpdThreads = 64;
 static_assert(kUpdThreads == 64 || kUpdThreads == 128 || kUpdThreads == 256, "lanes per block");
 constexpr int kPartsPerLane = kParts / kUpdThreads;
 
@@ -318,39 +305,116 @@ __device__ __forceinline__ void adamw_vec4(f32x4 &w, f32x4 g, f32x4 &m, f32x4 &v
 
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p) {
-#if RCS_UPD_NT
     return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
 }
 
 template <typename T>
 __device__ __forceinline__ void st_stream(T *p, T x) {
-#if RCS_UPD_NT
     __builtin_nontemporal_store(x, p);
-#else
-    *p = x;
-#endif
 }
 
-// Four consecutive floats of a lane: one 16-byte access when the array shares
-// w's 16-byte phase (VEC), else four 4-byte accesses (still streaming).
-template <bool VEC>
-__device__ __forceinline__ f32x4 ld4(const float *p) {
-    if constexpr (VEC) return ld_stream(reinterpret_cast<const f32x4 *>(p));
-    else return f32x4{ld_stream(p), ld_stream(p + 1), ld_stream(p + 2), ld_stream(p + 3)};
-}
+// An array among g, m, v at another 16-byte phase than w: its body xb (the
+// element matching w's first body element) lies q = 1-3 floats past a 16-byte
+// boundary, so lane i's four elements xb[4i .. 4i+3] straddle two aligned
+// vectors of the array. Every access stays a 16-byte aligned one: each lane
+// loads the aligned vector holding its first element (its positions q..3 are
+// the lane's first 4 - q elements) and takes the rest (positions 0..q-1 of the
+// next aligned vector) from the next lane's load through a cross-lane shift;
+// stores work the other way round, each lane writing the aligned vector that
+// holds its first element from the previous lane's last q elements and its
+// own first 4 - q. At the wave's edges, where the neighbouring lane is in
+// another wave, and at the ends of the body, the missing elements are loaded
+// or stored one by one (`own`, `lane0`, `first`). Any element a lane uses was
+// read by itself or by the next lane of its own wave before that wave's
+// stores; other waves only ever write positions this lane discards.
 
-template <bool VEC>
-__device__ __forceinline__ void st4(float *p, f32x4 x) {
-    if constexpr (VEC) {
-        st_stream(reinterpret_cast<f32x4 *>(p), x);
+// xb[4i .. 4i+3] for vector ic (i clamped to the body). first: ic is vector 0
+// and the aligned vector holding xb[0] starts before the array (head < q):
+// the lane's elements of it are read one by one. own: the next lane does not hold the next aligned vector (this is
+// the wave's last lane or the body's last vector): read positions 0..q-1 of it
+// one by one. Every lane of the wave must call this (cross-lane shifts).
+__device__ __forceinline__ f32x4 ld_shifted(const float *__restrict__ xb, int q, int64_t ic,
+                                            bool first, bool own) {
+    f32x4 a;
+    if (first) {
+        a = f32x4{0.f, 0.f, 0.f, 0.f};
+        a.w = ld_stream(xb + 3 - q);
+        if (q <= 2) a.z = ld_stream(xb + 2 - q);
+        if (q == 1) a.y = ld_stream(xb);
     } else {
-        st_stream(p, x.x);
-        st_stream(p + 1, x.y);
-        st_stream(p + 2, x.z);
-        st_stream(p + 3, x.w);
+        a = ld_stream(reinterpret_cast<const f32x4 *>(xb - q) + ic);
+    }
+    float b0 = __shfl_down(a.x, 1, kWave);
+    float b1 = __shfl_down(a.y, 1, kWave);
+    float b2 = __shfl_down(a.z, 1, kWave);
+    if (own) {
+        const float *p = xb + 4 * ic + 4 - q;
+        b0 = ld_stream(p);
+        if (q >= 2) b1 = ld_stream(p + 1);
+        if (q == 3) b2 = ld_stream(p + 2);
+    }
+    return q == 1 ? f32x4{a.y, a.z, a.w, b0} : q == 2 ? f32x4{a.z, a.w, b0, b1}
+                                                     : f32x4{a.w, b0, b1, b2};
+}
+
+// Writes r to xb[4i .. 4i+3] when active (i < n4). lane0: the wave's first
+// lane, whose previous lane is in another wave: its first 4 - q elements are
+// written one by one. own: as for ld_shifted, its last q elements are written
+// one by one. Those one-by-one writes fill part of a 16-byte vector that a
+// neighbouring wave fills the rest of; they are plain (cache-retained) stores
+// so that the two halves meet in the L2 cache rather than reaching memory as
+// partial writes (measured at the ANDREA-120M size with only v off w's phase:
+// 633-636 us/step against 650-656 with streaming stores there, 614-620 with v
+// at w's phase). Every lane of the wave must call this (cross-lane shifts).
+__device__ __forceinline__ void st_shifted(float *__restrict__ xb, int q, int64_t i, f32x4 r,
+                                           bool active, bool lane0, bool own) {
+    const float p1 = __shfl_up(r.y, 1, kWave);
+    const float p2 = __shfl_up(r.z, 1, kWave);
+    const float p3 = __shfl_up(r.w, 1, kWave);
+    if (!active) return;
+    float *p = xb + 4 * i;
+    if (!lane0) {
+        const f32x4 x = q == 1 ? f32x4{p3, r.x, r.y, r.z}
+                               : q == 2 ? f32x4{p2, p3, r.x, r.y} : f32x4{p1, p2, p3, r.x};
+        st_stream(reinterpret_cast<f32x4 *>(xb - q) + i, x);
+    } else {
+        p[0] = r.x;
+        if (q <= 2) p[1] = r.y;
+        if (q == 1) p[2] = r.z;
+    }
+    if (own) {
+        if (q == 3) {
+            p[1] = r.y;
+            p[2] = r.z;
+        } else if (q == 2) {
+            p[2] = r.z;
+        }
+        p[3] = r.w;
+    }
+}
+
+// Phases of w, g, m, v relative to the 16-byte aligned body, in floats
+// (0 = at the body's phase).
+struct Phases {
+    int w, g, m, v;
+};
+
+// Four elements of an array's body per lane: an aligned vector (VEC: the
+// array is at the body's 16-byte phase) or a shifted one.
+template <bool VEC>
+__device__ __forceinline__ f32x4 load4(const float *__restrict__ xb, int q, int64_t ic,
+                                       int head, bool own) {
+    if constexpr (VEC) return ld_stream(reinterpret_cast<const f32x4 *>(xb) + ic);
+    else return ld_shifted(xb, q, ic, ic == 0 && head < q, own);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void store4(float *__restrict__ xb, int q, int64_t i, f32x4 r,
+                                       bool active, bool lane0, bool own) {
+    if constexpr (VEC) {
+        if (active) st_stream(reinterpret_cast<f32x4 *>(xb) + i, r);
+    } else {
+        st_shifted(xb, q, i, r, active, lane0, own);
     }
 }
 
@@ -367,31 +431,35 @@ __device__ __forceinline__ void st4(float *p, f32x4 x) {
 // per-wave float64 square root and division cost more than the launch (one
 // wave per block: 529.7 against 552.2 us for the update at the ANDREA-120M
 // size, measured in one process).
-// w's body is 16-byte aligned (the head is w's); GV, MV, VV say whether g, m
-// and v share w's 16-byte phase and so take one 16-byte access per lane, or
-// lie at another and take four 4-byte accesses (ld4 / st4).
-template <bool FOLD, bool GV, bool MV, bool VV>
-__device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *__restrict__ gf,
+// w, g, m, v point `head` (0-63) elements past the arrays' starts, where the
+// body begins; the anchor array among w, m, v (the host's choice) has its body
+// on a 16-byte (normally 256-byte) boundary, and WV, GV, MV, VV say which
+// arrays share its 16-byte phase (aligned vectors) rather than lying ph.*
+// floats past it (shifted vectors; kUpdThreads is one wave).
+template <bool FOLD, bool WV, bool GV, bool MV, bool VV>
+__device__ __forceinline__ void update_body(float *__restrict__ wf, const float *__restrict__ gf,
                                             float *__restrict__ mf, float *__restrict__ vf,
-                                            int64_t n, int head,
+                                            int64_t n, int head, Phases ph,
                                             const double *__restrict__ partials, int nparts,
                                             float clip, ClipScalars *__restrict__ sc,
                                             const StepScalars &h, double *lds) {
     const int64_t n4 = n >> 2;
     int64_t c = blockIdx.x;
-    if (RCS_UPD_REGIONS > 1) {  // bijection of [0, nblk): region b % k, position b / k
+    {  // bijection of [0, nblk): region b % k, position b / k
         const int64_t nblk = gridDim.x;
-        const int64_t k = RCS_UPD_REGIONS, q = nblk / k, r = nblk % k, x = c % k, j = c / k;
+        const int64_t k = kRegions, q = nblk / k, r = nblk % k, x = c % k, j = c / k;
         c = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
     }
     const int64_t i = c * kUpdThreads + threadIdx.x;
     double xp[kPartsPerLane];
     if constexpr (FOLD) load_partials(partials, nparts, xp);
     const int64_t ic = i < n4 ? i : n4 - 1;
-    f32x4 gr = ld4<GV>(gf + 4 * ic);
-    f32x4 wr = ld_stream(w + ic);
-    f32x4 mr = ld4<MV>(mf + 4 * ic);
-    f32x4 vr = ld4<VV>(vf + 4 * ic);
+    const int lane = (int)threadIdx.x & (kWave - 1);
+    const bool own = lane == kWave - 1 || ic == n4 - 1;
+    f32x4 gr = load4<GV>(gf, ph.g, ic, head, own);
+    f32x4 wr = load4<WV>(wf, ph.w, ic, head, own);
+    f32x4 mr = load4<MV>(mf, ph.m, ic, head, own);
+    f32x4 vr = load4<VV>(vf, ph.v, ic, head, own);
     ClipScalars cs;
     if constexpr (FOLD) {
         cs = final_reduce(xp, nparts, clip, lds);
@@ -401,15 +469,14 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *
     }
     if (!cs.apply) return;
     const float s = cs.scale;
-    if (i < n4) {
-        adamw_vec4(wr, gr, mr, vr, s, h);
-        st_stream(w + i, wr);
-        st4<MV>(mf + 4 * i, mr);
-        st4<VV>(vf + 4 * i, vr);
-    }
+    const bool active = i < n4;
+    if (active) adamw_vec4(wr, gr, mr, vr, s, h);
+    const bool lane0 = lane == 0;
+    store4<WV>(wf, ph.w, i, wr, active, lane0, own);
+    store4<MV>(mf, ph.m, i, mr, active, lane0, own);
+    store4<VV>(vf, ph.v, i, vr, active, lane0, own);
     // block 0: the head elements before the body (indices -head .. -1);
     // the last block: the n % 4 after the last vector
-    float *wf = reinterpret_cast<float *>(w);
     if (blockIdx.x == 0 && (int)threadIdx.x < head) {
         const int64_t k = (int64_t)threadIdx.x - head;
         float ww = wf[k], mm = mf[k], vv = vf[k];
@@ -428,46 +495,49 @@ __device__ __forceinline__ void update_body(f32x4 *__restrict__ w, const float *
     }
 }
 
-// a3 after grad_norm_final. w, g, m, v point `head` (0-63) elements past the
-// arrays' starts, at 16-byte boundaries; n counts from there.
+// a3 after grad_norm_final, all four arrays at one 16-byte phase. w, g, m, v
+// point `head` (0-63) elements past the arrays' starts, at 16-byte
+// boundaries; n counts from there.
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
-    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
     float *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false, true, true, true>(w, g, m, v, n, head, nullptr, 0, 0.0f,
-                                         const_cast<ClipScalars *>(sc), h, nullptr);
+    update_body<false, true, true, true, true>(w, g, m, v, n, head, Phases{0, 0, 0, 0}, nullptr,
+                                               0, 0.0f, const_cast<ClipScalars *>(sc), h,
+                                               nullptr);
 }
 
 // a2 + a3 in one kernel (small n).
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
-    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
     float *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
     float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true, true, true, true>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h,
-                                        lds);
+    update_body<true, true, true, true, true>(w, g, m, v, n, head, Phases{0, 0, 0, 0}, partials,
+                                              nparts, clip, sc_out, h, lds);
 }
 
-// The same two kernels when some of g, m, v lie at another 16-byte phase than
-// w (e.g. w a view into a flat parameter buffer at an odd offset, m and v
-// fresh allocations): w and the arrays at its phase keep 16-byte vectors, the
-// others take four 4-byte accesses per lane.
-template <bool GV, bool MV, bool VV>
+// The same two kernels when the arrays lie at more than one 16-byte phase
+// (e.g. w a view into a flat parameter buffer at an odd offset, m and v fresh
+// allocations): the arrays at the anchor's phase take aligned 16-byte
+// vectors, the others shifted ones.
+template <bool WV, bool GV, bool MV, bool VV>
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_mixed(
-    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
-    float *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
+    float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, int head, Phases ph, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false, GV, MV, VV>(w, g, m, v, n, head, nullptr, 0, 0.0f,
-                                   const_cast<ClipScalars *>(sc), h, nullptr);
+    update_body<false, WV, GV, MV, VV>(w, g, m, v, n, head, ph, nullptr, 0, 0.0f,
+                                       const_cast<ClipScalars *>(sc), h, nullptr);
 }
 
-template <bool GV, bool MV, bool VV>
+template <bool WV, bool GV, bool MV, bool VV>
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_mixed_fold(
-    f32x4 *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
-    float *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
-    float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
+    float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
+    float *__restrict__ v, int64_t n, int head, Phases ph, const double *__restrict__ partials,
+    int nparts, float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true, GV, MV, VV>(w, g, m, v, n, head, partials, nparts, clip, sc_out, h, lds);
+    update_body<true, WV, GV, MV, VV>(w, g, m, v, n, head, ph, partials, nparts, clip, sc_out, h,
+                                      lds);
 }
 
 // a3 for arrays that are not 4-byte aligned or too short for a head and one
@@ -484,17 +554,6 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_scalar(
         w[i] = ww;
         m[i] = mm;
         v[i] = vv;
-    }
-}
-
-__global__ __launch_bounds__(256) void fp32_div_sqrt_probe(const float *__restrict__ a,
-                                                           const float *__restrict__ b,
-                                                           float *__restrict__ q,
-                                                           float *__restrict__ r, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) {
-        q[i] = a[i] / b[i];
-        r[i] = __builtin_sqrtf(a[i]);
     }
 }
 
@@ -592,27 +651,52 @@ __global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, 
 // a4 (asynchronous form): copy w, m, v into one device snapshot laid out like
 // the step file's payload [w | m | v], so that the training stream can keep
 // updating w, m, v while the snapshot drains to the host on a copy stream.
-// Vector path: n % 4 == 0 and all pointers 16-byte aligned; lane i copies
-// snapshot vector i, taken from w, m or v by which third it falls in.
-// One wave per block here too: 452-463 us against 466-483 us with 256 lanes
-// for the 1.49 GB snapshot at the ANDREA-120M size.
-#ifndef RCS_SNAP_THREADS
-#define RCS_SNAP_THREADS 64
-#endif
-constexpr int kSnapThreads = RCS_SNAP_THREADS;
-__global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const f32x4 *__restrict__ w,
-                                                                  const f32x4 *__restrict__ m,
-                                                                  const f32x4 *__restrict__ v,
-                                                                  f32x4 *__restrict__ snap,
-                                                                  int64_t n4) {
-    const int64_t total = 3 * n4;
-    const int64_t stride = (int64_t)gridDim.x * kSnapThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kSnapThreads + threadIdx.x; i < total; i += stride) {
-        const f32x4 *src = (i < n4) ? w + i : (i < 2 * n4) ? m + (i - n4) : v + (i - 2 * n4);
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src), snap + i);
+// blockIdx.y picks the array (w, m, v) and its place snap + y n. Each part is
+// written in aligned 16-byte vectors from its first 16-byte boundary on
+// (block 0 also copies the 0-3 elements before that boundary and the 0-3
+// after the last vector). A source at another 16-byte phase than its
+// destination (an n not divisible by 4 puts the m and v parts there, and so
+// can a view) is read in aligned 16-byte vectors shifted across lanes, as the
+// update reads g, m, v at another phase than w (ld_shifted); ph holds that
+// phase in floats for each part. One vector per lane, one wave per block: 452-463 us against
+// 466-483 us with 256 lanes for the 1.49 GB snapshot at the ANDREA-120M size.
+// The host guarantees n >= 4 and 4-byte aligned pointers.
+constexpr int kSnapThreads = 64;
+static_assert(kSnapThreads == kWave, "the shifted loads assume one wave per block");
+struct SnapPhases {
+    int w, m, v;
+};
+__global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *__restrict__ w,
+                                                                  const float *__restrict__ m,
+                                                                  const float *__restrict__ v,
+                                                                  float *__restrict__ snap,
+                                                                  int64_t n, SnapPhases ph) {
+    const int y = blockIdx.y;
+    const float *src = y == 0 ? w : y == 1 ? m : v;
+    float *dst = snap + (int64_t)y * n;
+    const int head = (int)(((16u - (reinterpret_cast<uintptr_t>(dst) & 15u)) & 15u) >> 2);
+    const int q = y == 0 ? ph.w : y == 1 ? ph.m : ph.v;
+    const int64_t nb = n - head;
+    const int64_t nb4 = nb >> 2;
+    const int64_t i = (int64_t)blockIdx.x * kSnapThreads + threadIdx.x;
+    if (nb4 > 0 && (int64_t)blockIdx.x * kSnapThreads < nb4) {  // uniform per block
+        const int64_t ic = i < nb4 ? i : nb4 - 1;
+        const float *sb = src + head;
+        f32x4 x;
+        if (q == 0) x = ld_stream(reinterpret_cast<const f32x4 *>(sb) + ic);
+        else x = ld_shifted(sb, q, ic, ic == 0 && head < q, threadIdx.x == kWave - 1 || ic == nb4 - 1);
+        if (i < nb4) st_stream(reinterpret_cast<f32x4 *>(dst + head) + i, x);
+    }
+    if (blockIdx.x == 0) {
+        if ((int)threadIdx.x < head) dst[threadIdx.x] = src[threadIdx.x];
+        if ((int)threadIdx.x < (int)(nb & 3)) {
+            const int64_t k = head + (nb4 << 2) + threadIdx.x;
+            dst[k] = src[k];
+        }
     }
 }
 
+// The same copy for pointers off a 4-byte boundary or n < 4.
 __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restrict__ w,
                                                             const float *__restrict__ m,
                                                             const float *__restrict__ v,
@@ -636,9 +720,14 @@ __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restr
 
 namespace {
 
-struct Workspace {
+// Device memory the norm kernels write: the per-block partial sums and the
+// clip record the update reads.
+struct NormBuffers {
     double *partials = nullptr;      // kNormMaxBlocks float64
     ClipScalars *scalars = nullptr;  // one record
+};
+
+struct Workspace : NormBuffers {
     std::atomic<bool> has_norm{false};
 };
 
@@ -657,6 +746,8 @@ struct SnapshotSync {
 };
 std::map<std::pair<int, const void *>, SnapshotSync> g_snap;
 
+// Read without the lock on every step; the records themselves are guarded.
+std::atomic<bool> g_prof_on{false};
 struct Profile {
     bool on = false;
     int max_records = 0;
@@ -668,9 +759,23 @@ struct Profile {
     std::vector<hipEvent_t> ev;
 } g_prof;
 
+// The last (device, stream) a host thread used and its workspace; workspaces
+// live until the process ends, so the pointer stays valid. Saves the map
+// lookup under the library lock on every step of a training loop.
+struct WsCache {
+    int dev = -1;
+    hipStream_t stream = nullptr;
+    Workspace *ws = nullptr;
+};
+thread_local WsCache t_ws;
+
 int get_workspace(hipStream_t stream, Workspace **out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
+    if (t_ws.ws != nullptr && t_ws.dev == dev && t_ws.stream == stream) {
+        *out = t_ws.ws;
+        return RCS_OK;
+    }
     const WsKey key(dev, stream,
                     stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id());
     std::lock_guard<std::mutex> lk(g_mu);
@@ -689,6 +794,9 @@ int get_workspace(hipStream_t stream, Workspace **out) {
             reinterpret_cast<ClipScalars *>(base + (size_t)kNormMaxBlocks * sizeof(double));
     }
     *out = &it->second;
+    t_ws.dev = dev;
+    t_ws.stream = stream;
+    t_ws.ws = &it->second;
     return RCS_OK;
 }
 
@@ -718,13 +826,16 @@ int check_device_range(const void *p, int64_t bytes) {
     return RCS_OK;  // device memory without a reportable range: accepted, length unchecked
 }
 
-bool overlaps(const void *a, const void *b, int64_t bytes) {
+// Whether [a, a + a_bytes) and [b, b + b_bytes) share a byte.
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
     const char *x = static_cast<const char *>(a);
     const char *y = static_cast<const char *>(b);
-    return x < y + bytes && y < x + bytes;
+    return x < y + b_bytes && y < x + a_bytes;
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool overlaps(const void *a, const void *b, int64_t bytes) { return overlaps(a, bytes, b, bytes); }
+
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int norm_blocks(int64_t n) {
     const int64_t per_block = kNormChunk * 4;  // floats per block-iteration
@@ -737,8 +848,7 @@ int norm_blocks(int64_t n) {
 // First vector index the norm pass reads with cache-allocating loads.
 int64_t norm_nt_limit4(int64_t n) {
     const int64_t n4 = n >> 2;
-    if (RCS_NORM_CACHED_TAIL_BYTES < 0) return 0;
-    const int64_t tail4 = (int64_t)RCS_NORM_CACHED_TAIL_BYTES / 16;
+    const int64_t tail4 = kNormCachedTailBytes / 16;
     return n4 > tail4 ? n4 - tail4 : 0;
 }
 
@@ -757,7 +867,7 @@ int head_of(const void *p, int64_t n) {
 }
 
 // a1 alone. ev0 / ev1 (optional, profiling) take the kernel's start / end.
-void launch_partial(const float *g, int64_t n, float gscale, Workspace *ws, hipStream_t stream,
+void launch_partial(const float *g, int64_t n, float gscale, const NormBuffers *ws, hipStream_t stream,
                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     const int head = head_of(g, n);
     hipExtLaunchKernelGGL(grad_norm_partial, dim3(norm_blocks(n)), dim3(kNormThreads), 0, stream,
@@ -767,7 +877,7 @@ void launch_partial(const float *g, int64_t n, float gscale, Workspace *ws, hipS
 
 // a1 + a2. ev (optional, profiling): ev[0] takes the partial kernel's start,
 // ev[1] the final kernel's end.
-int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *ws,
+int launch_norm(const float *g, int64_t n, float gscale, float clip, const NormBuffers *ws,
                 hipStream_t stream, hipEvent_t *ev = nullptr) {
     launch_partial(g, n, gscale, ws, stream, ev ? ev[0] : nullptr);
     hipExtLaunchKernelGGL(grad_norm_final, dim3(1), dim3(kUpdThreads), 0, stream, nullptr,
@@ -779,16 +889,17 @@ int launch_norm(const float *g, int64_t n, float gscale, float clip, Workspace *
 // Whether the vector kernels do the final reduction themselves (two launches)
 // rather than after grad_norm_final (three): only while the launch it saves
 // costs more than the reduction at the head of every wave.
-bool fold_final(int64_t n) { return n <= (int64_t)RCS_FOLD_MAX_N; }
+bool fold_final(int64_t n) { return n <= kFoldMaxN; }
 
 // Arguments of the update kernels after the norm kernels.
 struct UpdateLaunch {
     dim3 grid;
-    f32x4 *w;
+    float *w;
     const float *g;
     float *m, *v;
     int64_t nb;
     int head;
+    Phases ph;
     bool fold;
     const double *partials;
     int nparts;
@@ -799,10 +910,10 @@ struct UpdateLaunch {
     hipEvent_t e2, e3;
 };
 
-template <bool GV, bool MV, bool VV>
+template <bool WV, bool GV, bool MV, bool VV>
 void launch_update(const UpdateLaunch &a) {
     const dim3 block(kUpdThreads);
-    if constexpr (GV && MV && VV) {
+    if constexpr (WV && GV && MV && VV) {
         if (a.fold)
             hipExtLaunchKernelGGL(adamw_update_vec_fold, a.grid, block, 0, a.stream, a.e2, a.e3, 0,
                                   a.w, a.g, a.m, a.v, a.nb, a.head, a.partials, a.nparts, a.clip,
@@ -812,29 +923,41 @@ void launch_update(const UpdateLaunch &a) {
                                   a.g, a.m, a.v, a.nb, a.head, (const ClipScalars *)a.sc, a.h);
     } else {
         if (a.fold)
-            hipExtLaunchKernelGGL(adamw_update_mixed_fold<GV, MV, VV>, a.grid, block, 0, a.stream,
-                                  a.e2, a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head, a.partials,
-                                  a.nparts, a.clip, a.sc, a.h);
+            hipExtLaunchKernelGGL(adamw_update_mixed_fold<WV, GV, MV, VV>, a.grid, block, 0,
+                                  a.stream, a.e2, a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head, a.ph,
+                                  a.partials, a.nparts, a.clip, a.sc, a.h);
         else
-            hipExtLaunchKernelGGL(adamw_update_mixed<GV, MV, VV>, a.grid, block, 0, a.stream, a.e2,
-                                  a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head,
+            hipExtLaunchKernelGGL(adamw_update_mixed<WV, GV, MV, VV>, a.grid, block, 0, a.stream,
+                                  a.e2, a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head, a.ph,
                                   (const ClipScalars *)a.sc, a.h);
     }
 }
 
+// The anchor of the update's body among the written arrays w, m, v: the one
+// whose 16-byte phase the most of them share (w unless m and v share a phase
+// that w does not), so that as few written arrays as possible take shifted
+// vectors. 0 = w, 1 = m, 2 = v.
+int anchor_of(uintptr_t wa, uintptr_t ma, uintptr_t va) {
+    const uintptr_t pw = wa & 15u, pm = ma & 15u, pv = va & 15u;
+    return (pm == pv && pw != pm) ? 1 : 0;
+}
+
 // The whole step a1..a3. Vector form (all four arrays 4-byte aligned, at
-// least 4 elements past w's head): the partial kernel, [grad_norm_final,] the
-// update kernel on w's aligned body, which also takes the head elements; g, m
-// and v at w's 16-byte phase are accessed as 16-byte vectors, the others four
-// floats per lane. Otherwise: partial, final, scalar update.
+// least 4 elements past the anchor's head): the partial kernel,
+// [grad_norm_final,] the update kernel on the body from the anchor's next
+// 256-byte boundary on, which also takes the head elements; arrays at the
+// anchor's 16-byte phase are accessed as aligned 16-byte vectors, the others
+// as shifted ones. Otherwise: partial, final, scalar update.
 // ev (optional, profiling): ev[0] / ev[1] take the start of the partial kernel
 // and the end of the last norm kernel, ev[2] / ev[3] the update's start / end.
 int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float clip,
-                const StepScalars &h, Workspace *ws, hipStream_t stream, hipEvent_t *ev) {
+                const StepScalars &h, const NormBuffers *ws, hipStream_t stream, hipEvent_t *ev) {
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
     const uintptr_t wa = reinterpret_cast<uintptr_t>(w), ga = reinterpret_cast<uintptr_t>(g);
     const uintptr_t ma = reinterpret_cast<uintptr_t>(m), va = reinterpret_cast<uintptr_t>(v);
-    const int head = ((ga | ma | va) & 3u) == 0 ? head_of(w, n) : -1;
+    const int anchor = anchor_of(wa, ma, va);
+    const float *anchor_ptr = anchor == 0 ? w : m;
+    const int head = ((wa | ga | ma | va) & 3u) == 0 ? head_of(anchor_ptr, n) : -1;
     if (head >= 0) {
         const bool fold = fold_final(n);
         if (fold) {
@@ -845,9 +968,9 @@ int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float c
             if (rc != RCS_OK) return rc;
         }
         UpdateLaunch a;
-        a.nb = n - head;  // elements from w's boundary on
+        a.nb = n - head;  // elements from the body's boundary on
         a.grid = dim3((unsigned)(((a.nb >> 2) + kUpdThreads - 1) / kUpdThreads));
-        a.w = reinterpret_cast<f32x4 *>(w + head);
+        a.w = w + head;
         a.g = g + head;
         a.m = m + head;
         a.v = v + head;
@@ -861,18 +984,28 @@ int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float c
         a.stream = stream;
         a.e2 = e2;
         a.e3 = e3;
-        const uintptr_t ph = wa & 15u;
-        const int mask = ((ga & 15u) == ph ? 4 : 0) | ((ma & 15u) == ph ? 2 : 0) |
-                         ((va & 15u) == ph ? 1 : 0);
-        switch (mask) {
-            case 7: launch_update<true, true, true>(a); break;
-            case 6: launch_update<true, true, false>(a); break;
-            case 5: launch_update<true, false, true>(a); break;
-            case 4: launch_update<true, false, false>(a); break;
-            case 3: launch_update<false, true, true>(a); break;
-            case 2: launch_update<false, true, false>(a); break;
-            case 1: launch_update<false, false, true>(a); break;
-            default: launch_update<false, false, false>(a); break;
+        // each array's phase in floats past the 16-byte boundary where the body starts
+        const uintptr_t hb = 4u * (uintptr_t)head;
+        a.ph.w = (int)(((wa + hb) & 15u) >> 2);
+        a.ph.g = (int)(((ga + hb) & 15u) >> 2);
+        a.ph.m = (int)(((ma + hb) & 15u) >> 2);
+        a.ph.v = (int)(((va + hb) & 15u) >> 2);
+        const int mask = (a.ph.w == 0 ? 8 : 0) | (a.ph.g == 0 ? 4 : 0) | (a.ph.m == 0 ? 2 : 0) |
+                         (a.ph.v == 0 ? 1 : 0);
+        switch (mask) {  // the anchor is at phase 0, so w, m or v always is
+            case 15: launch_update<true, true, true, true>(a); break;
+            case 14: launch_update<true, true, true, false>(a); break;
+            case 13: launch_update<true, true, false, true>(a); break;
+            case 12: launch_update<true, true, false, false>(a); break;
+            case 11: launch_update<true, false, true, true>(a); break;
+            case 10: launch_update<true, false, true, false>(a); break;
+            case 9: launch_update<true, false, false, true>(a); break;
+            case 8: launch_update<true, false, false, false>(a); break;
+            case 7: launch_update<false, true, true, true>(a); break;
+            case 6: launch_update<false, true, true, false>(a); break;
+            case 3: launch_update<false, false, true, true>(a); break;
+            case 2: launch_update<false, false, true, false>(a); break;
+            default: return RCS_EINVAL;  // unreachable: the anchor's own phase is 0
         }
     } else {
         const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
@@ -886,6 +1019,40 @@ int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float c
     return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
+bool valid_n(int64_t n) { return n >= 1 && n <= RCS_MAX_N; }
+
+// Host-side checks shared by the update entry points: sizes, scalars, every
+// array inside one device allocation of the current device, g apart from
+// w, m, v and those apart from each other.
+int validate_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t, float lr,
+                  float wd, float clip, float grad_scale) {
+    if (!valid_n(n) || t < 1) return RCS_EINVAL;
+    if (!std::isfinite(grad_scale) || !(grad_scale > 0.0f)) return RCS_EINVAL;
+    if (!std::isfinite(lr) || !std::isfinite(wd) || std::isnan(clip) || !(clip > 0.0f))
+        return RCS_EINVAL;
+    const int64_t bytes = 4 * n;
+    int rc;
+    if ((rc = check_device_range(w, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(g, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
+    if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
+    if (overlaps(w, g, bytes) || overlaps(w, m, bytes) || overlaps(w, v, bytes) ||
+        overlaps(g, m, bytes) || overlaps(g, v, bytes) || overlaps(m, v, bytes))
+        return RCS_EINVAL;
+    return RCS_OK;
+}
+
+// a0: bias corrections and decay in float64, each rounded once to float32.
+StepScalars host_scalars(int32_t t, float lr, float wd, float grad_scale) {
+    StepScalars h;
+    h.lr = lr;
+    h.bc1 = (float)(1.0 - std::pow(0.9, (double)t));
+    h.bc2 = (float)(1.0 - std::pow(0.999, (double)t));
+    h.decay = (float)(1.0 - (double)lr * (double)wd);
+    h.gscale = grad_scale;
+    return h;
+}
+
 void put_le32(unsigned char *p, int32_t x) {
     const uint32_t u = (uint32_t)x;
     for (int k = 0; k < 4; ++k) p[k] = (unsigned char)((u >> (8 * k)) & 0xffu);
@@ -896,8 +1063,6 @@ int32_t get_le32(const unsigned char *p) {
     for (int k = 0; k < 4; ++k) u |= (uint32_t)p[k] << (8 * k);
     return (int32_t)u;
 }
-
-bool valid_n(int64_t n) { return n >= 1 && n <= RCS_MAX_N; }
 
 }  // namespace
 
@@ -948,32 +1113,13 @@ int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int
 
 int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                           float lr, float wd, float clip, float grad_scale, hipStream_t stream) {
-    if (!valid_n(n) || t < 1) return RCS_EINVAL;
-    if (!std::isfinite(grad_scale) || !(grad_scale > 0.0f)) return RCS_EINVAL;
-    if (!std::isfinite(lr) || !std::isfinite(wd) || std::isnan(clip) || !(clip > 0.0f))
-        return RCS_EINVAL;
-    const int64_t bytes = 4 * n;
     int rc;
-    if ((rc = check_device_range(w, bytes)) != RCS_OK) return rc;
-    if ((rc = check_device_range(g, bytes)) != RCS_OK) return rc;
-    if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
-    if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
-    if (overlaps(w, g, bytes) || overlaps(w, m, bytes) || overlaps(w, v, bytes) ||
-        overlaps(g, m, bytes) || overlaps(g, v, bytes) || overlaps(m, v, bytes))
-        return RCS_EINVAL;
+    if ((rc = validate_step(w, g, m, v, n, t, lr, wd, clip, grad_scale)) != RCS_OK) return rc;
     Workspace *ws = nullptr;
     if ((rc = get_workspace(stream, &ws)) != RCS_OK) return rc;
-
-    // a0: host scalars, float64 then one rounding each.
-    StepScalars h;
-    h.lr = lr;
-    h.bc1 = (float)(1.0 - std::pow(0.9, (double)t));
-    h.bc2 = (float)(1.0 - std::pow(0.999, (double)t));
-    h.decay = (float)(1.0 - (double)lr * (double)wd);
-    h.gscale = grad_scale;
-
+    const StepScalars h = host_scalars(t, lr, wd, grad_scale);
     hipEvent_t *ev = nullptr;
-    {
+    if (g_prof_on.load(std::memory_order_acquire)) {
         std::lock_guard<std::mutex> lk(g_mu);
         if (g_prof.on && (g_prof.calls++ % g_prof.every) == 0 && g_prof.next < g_prof.max_records)
             ev = &g_prof.ev[4 * g_prof.next++];
@@ -1118,9 +1264,8 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
     if ((rc = check_device_range(m, bytes)) != RCS_OK) return rc;
     if ((rc = check_device_range(v, bytes)) != RCS_OK) return rc;
     if ((rc = check_device_range(snapshot, 3 * bytes)) != RCS_OK) return rc;
-    if (overlaps(snapshot, w, 3 * bytes) || overlaps(snapshot, m, 3 * bytes) ||
-        overlaps(snapshot, v, 3 * bytes) || overlaps(w, snapshot, bytes) ||
-        overlaps(m, snapshot, bytes) || overlaps(v, snapshot, bytes))
+    if (overlaps(snapshot, 3 * bytes, w, bytes) || overlaps(snapshot, 3 * bytes, m, bytes) ||
+        overlaps(snapshot, 3 * bytes, v, bytes))
         return RCS_EINVAL;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
@@ -1145,14 +1290,19 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
     }
     if (pending && hipStreamWaitEvent(compute_stream, ss->copied, 0) != hipSuccess)
         return RCS_EHIP;
-    if (n % 4 == 0 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(snapshot)) {
-        const int64_t total = 3 * (n >> 2);
-        const int64_t blocks = (total + kSnapThreads - 1) / kSnapThreads;  // one vector per lane
-        hipLaunchKernelGGL(ckpt_snapshot_vec, dim3((unsigned)blocks), dim3(kSnapThreads), 0,
-                           compute_stream,
-                           reinterpret_cast<const f32x4 *>(w), reinterpret_cast<const f32x4 *>(m),
-                           reinterpret_cast<const f32x4 *>(v), reinterpret_cast<f32x4 *>(snapshot),
-                           n >> 2);
+    if (n >= 4 && aligned4(w) && aligned4(m) && aligned4(v) && aligned4(snapshot)) {
+        const int64_t blocks = ((n >> 2) + kSnapThreads - 1) / kSnapThreads;  // one vector per lane
+        // each part's source phase relative to its destination's first 16-byte boundary
+        SnapPhases ph;
+        const float *src[3] = {w, m, v};
+        int *q[3] = {&ph.w, &ph.m, &ph.v};
+        for (int k = 0; k < 3; ++k) {
+            const uintptr_t d = reinterpret_cast<uintptr_t>(snapshot + (int64_t)k * n);
+            const uintptr_t head = ((16u - (d & 15u)) & 15u) >> 2;
+            *q[k] = (int)(((reinterpret_cast<uintptr_t>(src[k]) + 4u * head) & 15u) >> 2);
+        }
+        hipLaunchKernelGGL(ckpt_snapshot_vec, dim3((unsigned)blocks, 3), dim3(kSnapThreads), 0,
+                           compute_stream, w, m, v, snapshot, n, ph);
     } else {
         int64_t blocks = (3 * n + 255) / 256;
         if (blocks > 65536) blocks = 65536;
@@ -1191,6 +1341,7 @@ int ckpt_pack_wait(const float *snapshot) {
 
 int rcs_profile_enable(int on, int max_records, int every) {
     std::lock_guard<std::mutex> lk(g_mu);
+    g_prof_on.store(false, std::memory_order_release);
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
     g_prof.ev.clear();
     g_prof.on = false;
@@ -1209,6 +1360,7 @@ int rcs_profile_enable(int on, int max_records, int every) {
     }
     g_prof.max_records = max_records;
     g_prof.on = true;
+    g_prof_on.store(true, std::memory_order_release);
     return RCS_OK;
 }
 
@@ -1233,21 +1385,6 @@ int rcs_profile_read(double *norm_ms_total, double *update_ms_total, int64_t *st
     *update_ms_total = b;
     *steps = (int64_t)(ev.size() / 4);
     return RCS_OK;
-}
-
-int rcs_fp32_div_sqrt_probe(const float *a, const float *b, float *q, float *r, int64_t n,
-                            hipStream_t stream) {
-    if (n < 1 || n > RCS_MAX_N) return RCS_EINVAL;
-    const int64_t bytes = 4 * n;
-    int rc;
-    if ((rc = check_device_range(a, bytes)) != RCS_OK) return rc;
-    if ((rc = check_device_range(b, bytes)) != RCS_OK) return rc;
-    if ((rc = check_device_range(q, bytes)) != RCS_OK) return rc;
-    if ((rc = check_device_range(r, bytes)) != RCS_OK) return rc;
-    const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(fp32_div_sqrt_probe, dim3((unsigned)blocks), dim3(256), 0, stream, a, b, q,
-                       r, n);
-    return hipGetLastError() == hipSuccess ? RCS_OK : RCS_EHIP;
 }
 
 }  // extern "C"

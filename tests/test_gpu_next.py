@@ -150,6 +150,62 @@ def test_async_pack_equals_synchronous_pack_while_training_continues(dev, n):
     assert ob.tobytes() == bufs[k].numpy().tobytes()
 
 
+# (n, offsets of w, m, v and the snapshot in elements past a 512-byte boundary):
+# the snapshot's m and v parts start off a 16-byte boundary whenever n % 4 != 0,
+# and views put the sources at other phases still; n < 4 takes the scalar copy.
+SNAPSHOT_CASES = [(1, (0, 0, 0, 0)), (3, (1, 2, 3, 1)), (4, (0, 0, 0, 3)), (5, (0, 0, 0, 0)),
+                  (7, (3, 2, 1, 0)), (262_147, (0, 0, 0, 0)), (262_146, (1, 1, 1, 1)),
+                  (1_000_001, (2, 3, 0, 1)), (1_000_000, (0, 1, 2, 3))]
+
+
+@pytest.mark.parametrize("n,offs", SNAPSHOT_CASES)
+def test_async_pack_any_n_and_phase(dev, n, offs):
+    """The snapshot kernel's 16-byte path at every 4-byte phase of source and
+    destination: the async pack equals the synchronous pack of the same state,
+    and the elements around the snapshot are not written."""
+    W, M, V = (torch.zeros(n + 4, device=dev) for _ in range(3))
+    S = torch.full((3 * n + 8,), 7.0, device=dev)
+    w, m, v = (X[o:o + n] for X, o in zip((W, M, V), offs))
+    snap = S[offs[3]:offs[3] + 3 * n]
+    for x, seed in ((w, 1200), (m, 1201), (v, 1202)):
+        x.copy_(workloads.custom(seed, n, 1.0, device=dev))
+    nb = rcs.ckpt_bytes(n)
+    ref, buf = (torch.empty(nb, dtype=torch.uint8, pin_memory=True) for _ in range(2))
+    rcs.ckpt_pack(9, w, m, v, ref)
+    copy_stream = torch.cuda.Stream()
+    rcs.ckpt_pack_async(9, w, m, v, snap, buf, compute_stream=torch.cuda.current_stream(),
+                        copy_stream=copy_stream)
+    rcs.ckpt_pack_wait(snap)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref), (n, offs)
+    assert (S[:offs[3]] == 7.0).all() and (S[offs[3] + 3 * n:] == 7.0).all()
+
+
+def test_async_pack_from_one_arena(dev):
+    """w, m, v and the snapshot carved one after another from one allocation
+    ([w | m | v | snapshot]): adjacent but disjoint ranges are accepted, and an
+    overlapping snapshot is refused."""
+    n = 100_003
+    A = torch.empty(6 * n, device=dev)
+    w, m, v, snap = A[:n], A[n:2 * n], A[2 * n:3 * n], A[3 * n:]
+    for x, seed in ((w, 1210), (m, 1211), (v, 1212)):
+        x.copy_(workloads.custom(seed, n, 1.0, device=dev))
+    nb = rcs.ckpt_bytes(n)
+    ref, buf = (torch.empty(nb, dtype=torch.uint8, pin_memory=True) for _ in range(2))
+    rcs.ckpt_pack(4, w, m, v, ref)
+    copy_stream = torch.cuda.Stream()
+    rcs.ckpt_pack_async(4, w, m, v, snap, buf, compute_stream=torch.cuda.current_stream(),
+                        copy_stream=copy_stream)
+    rcs.ckpt_pack_wait(snap)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
+    B = torch.empty(5 * n, device=dev)  # the snapshot's first third is v
+    with pytest.raises(rcs.RcsError) as e:
+        rcs.ckpt_pack_async(4, B[:n], B[n:2 * n], B[2 * n:3 * n], B[2 * n:], buf,
+                            compute_stream=torch.cuda.current_stream(), copy_stream=copy_stream)
+    assert e.value.status == rcs.EINVAL
+
+
 def _unpacked(buf, n):
     raw = buf.numpy()
     return [torch.from_numpy(raw[8 + 4 * j * n: 8 + 4 * (j + 1) * n].view(np.float32).copy())

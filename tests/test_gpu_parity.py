@@ -7,6 +7,9 @@ bit-identical unless the two float64 norms round the clip factor apart);
 headers, layout and packed bytes bit-exact; a packed-and-resumed run
 bit-identical to the straight run.
 """
+import ctypes
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -46,6 +49,20 @@ def _check_state(w, m, v, ow, om, ov, ctx):
 
 # ---------------------------------------------------------------- device arithmetic
 
+def _fp32_div_sqrt(a, b):
+    """q = a / b, r = sqrtf(a) on the device, from the tests' probe library
+    (tests/native/fp32_probe.hip, built by __graft_entry__.build())."""
+    path = os.path.join(os.path.dirname(__file__), "native", "libfp32probe.so")
+    L = ctypes.CDLL(path)
+    L.fp32_div_sqrt_probe.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p]
+    L.fp32_div_sqrt_probe.restype = ctypes.c_int
+    q, r = torch.empty_like(a), torch.empty_like(a)
+    assert L.fp32_div_sqrt_probe(a.data_ptr(), b.data_ptr(), q.data_ptr(), r.data_ptr(),
+                                 a.numel(), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    return q, r
+
+
 def test_fp32_divide_and_sqrt_are_correctly_rounded(dev):
     rng = np.random.default_rng(0)
     n = 1 << 20
@@ -56,8 +73,7 @@ def test_fp32_divide_and_sqrt_are_correctly_rounded(dev):
     b[n // 4: n // 2] = np.ldexp(rng.random(n // 4) + 0.5, e[n // 4: n // 2]).astype(np.float32)
     a[:64] = np.float32(1.4e-45) * np.arange(1, 65, dtype=np.float32)  # subnormal numerators
     b[b == 0] = 1.0
-    q, r = rcs.fp32_div_sqrt_probe(torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev))
-    torch.cuda.synchronize()
+    q, r = _fp32_div_sqrt(torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev))
     with np.errstate(all="ignore"):
         q_ref = a / b
         r_ref = np.sqrt(np.abs(a))
@@ -174,11 +190,11 @@ def test_update_parity_ragged_sizes(dev, n):
 # 256-byte boundary (64 - offset elements: bodies of exactly 4 and 7 behind a
 # 63-element head, head and tail in one block), or to the next 16-byte one when
 # fewer than 4 elements would follow (heads of 1-3, bodies of 4, 5 and 7); g, m
-# and v may sit at other 256-byte phases (1, 5, 9, 65). Arrays among g, m, v
-# whose offset differs from w's modulo 4 take four 4-byte accesses per lane
-# in the vector kernels (adamw_update_mixed: each of the seven combinations of
-# which arrays differ appears here). Both
-# final-reduction forms. Views too short for either head take the scalar
+# and v may sit at other 256-byte phases (1, 5, 9, 65). Arrays whose offset
+# differs from the anchor's modulo 4 (the anchor is w, or m when m and v share
+# a phase w does not) take shifted 16-byte vectors in the vector kernels
+# (adamw_update_mixed: every reachable combination appears here, in both
+# final-reduction forms). Views too short for either head take the scalar
 # kernels.
 UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3), 50_001),
                    ((1, 1, 1, 1), 67), ((1, 1, 1, 1), 70), ((2, 2, 2, 2), 66),
@@ -190,7 +206,13 @@ UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3)
                    ((1, 2, 0, 3), 50_001), ((0, 0, 0, 1), 4099), ((1, 0, 0, 0), 50_001),
                    ((0, 1, 2, 3), 8_388_608), ((3, 3, 0, 3), 12_800_003), ((2, 2, 2, 0), 66),
                    ((1, 1, 2, 1), 70), ((1, 1, 0, 2), 50_001), ((1, 0, 1, 2), 4099),
-                   ((3, 0, 1, 3), 12_800_003), ((2, 2, 2, 2), 5)]
+                   ((3, 0, 1, 3), 12_800_003), ((2, 2, 2, 2), 5),
+                   # m and v sharing a phase w does not: the body is anchored on m
+                   # and w takes the shifted vectors (a 1-vector body with a tail too)
+                   ((1, 2, 0, 0), 50_001), ((1, 2, 0, 0), 12_800_003), ((1, 0, 0, 0), 8_388_611),
+                   ((1, 0, 0, 0), 6), ((2, 0, 0, 0), 5), ((0, 1, 2, 0), 4099),
+                   ((0, 0, 0, 1), 12_800_003), ((1, 1, 0, 2), 8_388_611),
+                   ((1, 0, 1, 2), 12_800_003), ((0, 1, 2, 3), 12_800_003)]
 
 
 @pytest.mark.parametrize("offs,n", UNALIGNED_CASES)
@@ -407,8 +429,10 @@ def test_resume_without_the_full_state_differs(dev, lost):
 
 
 def test_resume_bit_identical_andrea12m(dev):
+    """ANDREA-12M's cadence: 200 updates, resumed from the step-100 pack."""
     wl = workloads.WORKLOADS["andrea12m"]
-    _straight_vs_resumed(dev, wl, 20, 10)
+    _, _, _, packed = _straight_vs_resumed(dev, wl, wl.steps, 100)
+    assert packed.numel() == 153_600_008
 
 
 def test_resume_bit_identical_stress_full_size(dev):
@@ -419,14 +443,16 @@ def test_resume_bit_identical_stress_full_size(dev):
 
 # ---------------------------------------------------------------- near the int32 limit
 
-@pytest.mark.timeout(600)
-def test_flat2e9_sampled_parity_and_pack(dev):
-    """n = 2e9 (32 GB of w, g, m, v): two updates in the launch configuration
-    the benchmark times; the float64 norm is checked against the oracle's norm
-    streamed over all 2e9 gradients, w, m, v on 1 Mi-element chunks spread
-    over the vector (the first and the last included), then one 24 GB pack:
-    header and sampled byte ranges, and an unpack that restores w, m, v bit
-    for bit."""
+@pytest.mark.timeout(800)
+def test_flat2e9_all_10_steps_sampled_parity_and_pack(dev):
+    """n = 2e9 (32 GB of w, g, m, v) as configured: all 10 updates in the
+    launch configuration the benchmark times. Every step the float64 norm is
+    checked against the oracle's norm streamed over all 2e9 gradients, and 14
+    sampled 1 Mi-element chunks (the first and the last included) are carried
+    through the oracle's elementwise update with the clip factor from that
+    streamed norm; w, m, v on them within 2 ulp after every step. Then one
+    24 GB pack after step 10: header and sampled byte ranges, and an unpack
+    into fresh arrays that restores w, m, v bit for bit."""
     wl = workloads.WORKLOADS["flat2e9"]
     n = wl.n
     chunk = 1 << 20
@@ -435,40 +461,40 @@ def test_flat2e9_sampled_parity_and_pack(dev):
     w = workloads.init_params(wl, device=dev)
     m, v = workloads.zeros_like_state(n, device=dev)
     g = torch.empty(n, device=dev)
-    workloads.grads(wl, 1, device=dev, out=g)
-    rcs.adamw_clip_step(w, g, m, v, 1, wl.lr, wl.wd, wl.clip)
-    workloads.grads(wl, 2, device=dev, out=g)
-    before = {o: [_host(x[o:o + chunk]).copy() for x in (w, g, m, v)] for o in offs}
-    rcs.adamw_clip_step(w, g, m, v, 2, wl.lr, wl.wd, wl.clip)
-    gpu_norm = _gpu_norm()
-    acc = oracle.NormAccumulator()
-    step = 1 << 28
-    for lo in range(0, n, step):
-        acc.add(_host(g[lo:min(lo + step, n)]))
-    onorm = acc.norm()
-    print(f"flat2e9: norm gpu {gpu_norm!r} oracle {onorm!r}", flush=True)
-    assert abs(gpu_norm - onorm) <= NORM_RTOL * onorm
-    s = oracle.clip_scale(onorm, wl.clip)
-    bc1, bc2, decay = oracle.scalars(2, wl.lr, wl.wd)
-    for o in offs:
-        ow, og, om, ov = before[o]
-        oracle.adamw_elems(ow, og, om, ov, float(s), float(bc1), float(bc2), float(decay), wl.lr)
-        _check_state(w[o:o + chunk], m[o:o + chunk], v[o:o + chunk], ow, om, ov,
-                     f"flat2e9 chunk at {o}")
+    state = {o: [_host(x[o:o + chunk]).copy() for x in (w, m, v)] for o in offs}
+    for t in range(1, wl.steps + 1):
+        workloads.grads(wl, t, device=dev, out=g)
+        gs = {o: _host(g[o:o + chunk]).copy() for o in offs}
+        rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
+        gpu_norm = _gpu_norm()
+        acc = oracle.NormAccumulator()
+        for lo in range(0, n, 1 << 28):
+            acc.add(_host(g[lo:min(lo + (1 << 28), n)]))
+        onorm = acc.norm()
+        print(f"flat2e9 t={t}: norm gpu {gpu_norm!r} oracle {onorm!r}", flush=True)
+        assert abs(gpu_norm - onorm) <= NORM_RTOL * onorm
+        s = oracle.clip_scale(onorm, wl.clip)
+        bc1, bc2, decay = oracle.scalars(t, wl.lr, wl.wd)
+        for o in offs:
+            ow, om, ov = state[o]
+            oracle.adamw_elems(ow, gs[o], om, ov, float(s), float(bc1), float(bc2), float(decay),
+                               wl.lr)
+            _check_state(w[o:o + chunk], m[o:o + chunk], v[o:o + chunk], ow, om, ov,
+                         f"flat2e9 t={t} chunk at {o}")
     del g
     nb = rcs.ckpt_bytes(n)
     assert nb == 24_000_000_008
     buf = _pinned(nb)
-    rcs.ckpt_pack(2, w, m, v, buf)
+    rcs.ckpt_pack(wl.steps, w, m, v, buf)
     torch.cuda.synchronize()
     raw = buf.numpy()
-    assert oracle.ckpt_header(raw[:8].copy()) == (oracle.OK, 2, n)
-    for o in (offs[0], offs[len(offs) // 2], offs[-1]):
+    assert oracle.ckpt_header(raw[:8].copy()) == (oracle.OK, wl.steps, n)
+    for o in offs:
         for k, x in enumerate((w, m, v)):
             lo = 8 + 4 * k * n + 4 * o
             assert raw[lo:lo + 4 * chunk].tobytes() == _host(x[o:o + chunk]).tobytes()
     w2, m2, v2 = (torch.empty(n, device=dev) for _ in range(3))
-    assert rcs.ckpt_unpack(buf, w2, m2, v2) == 2
+    assert rcs.ckpt_unpack(buf, w2, m2, v2) == wl.steps
     torch.cuda.synchronize()
     for a, b in ((w, w2), (m, m2), (v, v2)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
@@ -476,26 +502,37 @@ def test_flat2e9_sampled_parity_and_pack(dev):
 
 # ---------------------------------------------------------------- whole runs at full size
 
-def _full_run(dev, wl, check_every):
+def _full_run(dev, wl, check_every, resume_at=None):
+    """All wl.steps updates on the GPU beside the oracle's straight run: the
+    norm within 1e-12 every step, w, m, v within 2 ulp every check_every steps
+    and at every pack, packed bytes equal to the oracle's pack of its own state
+    whenever the two states are bit-identical. resume_at: at that step the GPU
+    state is packed, the device arrays dropped, fresh NaN-filled ones unpacked
+    from the bytes, and the run continues from them (t = step + 1) while the
+    oracle goes straight on, so every later check compares a resumed GPU run
+    with a run that never stopped."""
     n = wl.n
     w = workloads.init_params(wl, device=dev)
     m, v = workloads.zeros_like_state(n, device=dev)
     ow, om, ov = _host(w).copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
     g = torch.empty(n, device=dev)
     worst = 0
-    for t in range(1, wl.steps + 1):
+    t = 0
+    while t < wl.steps:
+        t += 1
         workloads.grads(wl, t, device=dev, n=n, out=g)
         rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip)
         gn = _gpu_norm()
         rc, on = oracle.adamw_clip_step(ow, _host(g), om, ov, t, wl.lr, wl.wd, wl.clip)
         assert rc == oracle.OK and abs(gn - on) <= NORM_RTOL * on, (t, gn, on)
-        if t % check_every == 0 or t == wl.steps:
+        packing = t in wl.pack_at or t == resume_at
+        if t % check_every == 0 or t == wl.steps or packing:
             for name, a, b in (("w", w, ow), ("m", m, om), ("v", v, ov)):
                 d = max_ulp(_host(a), b)
                 worst = max(worst, d)
                 assert d <= ULP_TOL, f"{wl.name} t={t}: {name} max ulp distance {d}"
             print(f"{wl.name}: step {t} within {worst} ulp", flush=True)
-        if t in wl.pack_at:
+        if packing:
             buf = _pinned(rcs.ckpt_bytes(n))
             rcs.ckpt_pack(t, w, m, v, buf)
             torch.cuda.synchronize()
@@ -503,19 +540,37 @@ def _full_run(dev, wl, check_every):
             if worst == 0:  # identical states pack to identical bytes
                 _, ob = oracle.ckpt_pack(t, ow, om, ov)
                 assert buf.numpy().tobytes() == ob.tobytes()
+            if t == resume_at:
+                del w, m, v
+                w, m, v = (torch.full((n,), float("nan"), device=dev) for _ in range(3))
+                t = rcs.ckpt_unpack(buf, w, m, v)
+                assert t == resume_at
+                print(f"{wl.name}: resumed from the step-{t} pack", flush=True)
     return worst
 
 
 @pytest.mark.timeout(300)
 def test_andrea12m_all_200_steps_against_oracle(dev):
+    """ANDREA-12M as configured: 200 updates, a checkpoint every 100; the run
+    resumes from its step-100 pack and its step-200 pack equals the oracle's."""
     wl = workloads.WORKLOADS["andrea12m"]
-    print("andrea12m worst ulp:", _full_run(dev, wl, 20))
+    print("andrea12m worst ulp:", _full_run(dev, wl, 20, resume_at=100))
 
 
 @pytest.mark.timeout(600)
 def test_andrea120m_all_100_steps_against_oracle(dev):
     wl = workloads.WORKLOADS["andrea120m"]
     print("andrea120m worst ulp:", _full_run(dev, wl, 25))
+
+
+@pytest.mark.timeout(600)
+def test_stress_all_200_steps_against_oracle_resumed_at_100(dev):
+    """The subnormal-heavy stress workload as configured: 200 updates with
+    gradients N(0, 1), 5% exact zeros and 0.1% near FLT_MIN (the clip fires
+    every step, s ~ 9e-5, so g * s and the moments go subnormal), packed,
+    dropped and unpacked at step 100, against the oracle's straight run."""
+    wl = workloads.WORKLOADS["andrea120m_stress"]
+    print("stress worst ulp:", _full_run(dev, wl, 25, resume_at=100))
 
 
 @pytest.mark.timeout(600)
