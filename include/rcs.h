@@ -51,9 +51,11 @@ enum rcs_status {
 const char *rcs_strerror(int status);
 
 /* Allocates the workspace of (device, stream) ahead of time so that no later
- * call allocates. Optional; needed before capturing adamw_clip_step (or the
- * norm and clip calls) on that stream into a graph: the capture then holds
- * only the kernels, with t and the hyper-parameters fixed at capture. */
+ * call allocates, and looks up the device's copy of the static array that
+ * adamw_clip_step_noalloc uses. Optional; needed before capturing
+ * adamw_clip_step (or the norm and clip calls) on that stream into a graph:
+ * the capture then holds only the kernels, with t and the hyper-parameters
+ * fixed at capture. */
 int rcs_init(int device, hipStream_t stream);
 
 /*
@@ -117,6 +119,30 @@ int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int
  */
 int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                           float lr, float wd, float clip, float grad_scale, hipStream_t stream);
+
+/*
+ * adamw_clip_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as adamw_clip_step (bit for bit), but
+ * the norm pass's partial sums and the clip record live in a static device
+ * array of 4 KiB compiled into the library (one per GPU, held until the
+ * process ends) instead of the per-(device, stream) workspace, and the call
+ * makes no allocation of any kind. The array's device address is looked up
+ * once per GPU, by rcs_init or else by the first call on that GPU. Every n
+ * from 1 to RCS_MAX_N fits in it (the norm pass never has more than 256
+ * blocks); a larger n is RCS_EINVAL as for adamw_clip_step.
+ * norm_out (may be NULL): pinned host or current-device memory that receives
+ * the float64 pre-clip norm in stream order (this call does not update what
+ * last_grad_norm reports).
+ * All calls on one GPU share the array: two calls whose work overlaps on the
+ * device (different streams without ordering between them) race on it and may
+ * corrupt each other's norm; order them, or use adamw_clip_step. Nothing in
+ * the array needs clearing: every call writes the partials and the record
+ * before reading them.
+ */
+int adamw_clip_step_noalloc(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
+                            float lr, float wd, float clip, double *norm_out,
+                            hipStream_t stream);
 
 /*
  * The pre-clip global norm alone: sqrt(sum_i (double)g[i]^2), same kernels and

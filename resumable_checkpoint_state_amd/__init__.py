@@ -19,7 +19,7 @@ from ._build import LIB as LIB_PATH
 from ._build import build
 
 __all__ = [
-    "RcsError", "adamw_clip_step", "adamw_clip_step_accum", "grad_clip_inplace", "grad_zero", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
+    "RcsError", "adamw_clip_step", "adamw_clip_step_noalloc", "adamw_clip_step_accum", "grad_clip_inplace", "grad_zero", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
     "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read",
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
     "ckpt_pack_async", "ckpt_pack_wait", "CkptWriter", "StepFileCheckpointer",
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.rcs_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     L.rcs_profile_read.restype = ctypes.c_int
+    L.adamw_clip_step_noalloc.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, vp,
+                                          vp]
+    L.adamw_clip_step_noalloc.restype = ctypes.c_int
     L.adamw_clip_step_accum.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, f32, vp]
     L.adamw_clip_step_accum.restype = ctypes.c_int
     L.grad_clip_inplace.argtypes = [f32p, i64, f32, vp]
@@ -169,6 +172,20 @@ def adamw_clip_step(w, g, m, v, t: int, lr: float, wd: float, clip: float, strea
     args = (wp, _dev_f32(g, "g", n, cur), _dev_f32(m, "m", n, cur), _dev_f32(v, "v", n, cur))
     _check(lib().adamw_clip_step(*args, n, int(t), float(lr), float(wd), float(clip),
                                  _stream(stream, cur)), "adamw_clip_step")
+
+
+def adamw_clip_step_noalloc(w, g, m, v, t: int, lr: float, wd: float, clip: float,
+                            norm_out: torch.Tensor | None = None, stream=None) -> None:
+    """adamw_clip_step without any allocation: the norm buffers are the
+    library's static device array (shared by every call on the GPU, so calls
+    must not overlap on the device). norm_out: optional 1-element float64
+    device or pinned host tensor that receives the pre-clip norm."""
+    n, wp = w.numel(), _dev_f32(w, "w")
+    cur = w.get_device()
+    args = (wp, _dev_f32(g, "g", n, cur), _dev_f32(m, "m", n, cur), _dev_f32(v, "v", n, cur))
+    np_ = None if norm_out is None else _norm_out(norm_out).data_ptr()
+    _check(lib().adamw_clip_step_noalloc(*args, n, int(t), float(lr), float(wd), float(clip),
+                                         np_, _stream(stream, cur)), "adamw_clip_step_noalloc")
 
 
 def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: float,

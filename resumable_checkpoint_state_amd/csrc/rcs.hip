@@ -713,6 +713,15 @@ __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restr
 
 }  // namespace
 
+// Device scratch of adamw_clip_step_noalloc, for callers that cannot allocate:
+// the norm pass's per-block float64 partial sums (at most kNormMaxBlocks of
+// them, 2 KiB, whatever n is) followed by the clip record. Each GPU holds one
+// copy until the process ends. Host code never passes this name to a kernel
+// (on the host it only stands in for the symbol): it takes the copy's device
+// address once per device with hipGetSymbolAddress and passes that.
+constexpr size_t kScratchBytes = 4096;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 #include <thread>
 #include <tuple>
 
@@ -736,6 +745,36 @@ std::mutex g_mu;
 // every host thread, so under that handle the thread is part of the key.
 using WsKey = std::tuple<int, hipStream_t, std::thread::id>;
 std::map<WsKey, Workspace> g_ws;
+
+// Device address of each GPU's copy of `scratch` (null until looked up).
+constexpr int kMaxDevices = 256;
+std::atomic<char *> g_scratch_addr[kMaxDevices];
+constexpr size_t kScratchRecordOffset = (size_t)kNormMaxBlocks * sizeof(double);
+static_assert(kScratchRecordOffset % alignof(ClipScalars) == 0, "record alignment");
+static_assert(kScratchRecordOffset + sizeof(ClipScalars) <= kScratchBytes, "scratch size");
+
+// The address of device dev's copy of `scratch`; dev must be the current
+// device. Looked up once per device (rcs_init, else the first
+// adamw_clip_step_noalloc on it); no allocation.
+int scratch_address(int dev, char **out) {
+    if (dev < 0 || dev >= kMaxDevices) return RCS_EINVAL;
+    char *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void *q = nullptr;
+            if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+                (void)hipGetLastError();
+                return RCS_EHIP;
+            }
+            p = static_cast<char *>(q);
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RCS_OK;
+}
 
 // Per snapshot buffer: `ready` is recorded on the compute stream after the
 // snapshot kernel, `copied` on the copy stream after the device-to-host copy.
@@ -1053,6 +1092,19 @@ StepScalars host_scalars(int32_t t, float lr, float wd, float grad_scale) {
     return h;
 }
 
+// A norm destination: pinned host memory, or 8 bytes of device memory of
+// device dev.
+int check_norm_out(const double *p, int dev) {
+    hipPointerAttribute_t pa;
+    if (hipPointerGetAttributes(&pa, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return RCS_EINVAL;
+    }
+    if (pa.type == hipMemoryTypeHost) return RCS_OK;
+    if (pa.type == hipMemoryTypeDevice && pa.device != dev) return RCS_EINVAL;
+    return check_device_range(p, sizeof(double));
+}
+
 void put_le32(unsigned char *p, int32_t x) {
     const uint32_t u = (uint32_t)x;
     for (int k = 0; k < 4; ++k) p[k] = (unsigned char)((u >> (8 * k)) & 0xffu);
@@ -1101,7 +1153,9 @@ int rcs_init(int device, hipStream_t stream) {
         return RCS_EINVAL;
     }
     Workspace *ws = nullptr;
-    const int rc = get_workspace(stream, &ws);
+    int rc = get_workspace(stream, &ws);
+    char *scr = nullptr;
+    if (rc == RCS_OK) rc = scratch_address(device, &scr);
     (void)hipSetDevice(prev);
     return rc;
 }
@@ -1127,6 +1181,31 @@ int adamw_clip_step_accum(float *w, const float *g, float *m, float *v, int64_t 
     rc = launch_step(w, g, m, v, n, clip, h, ws, stream, ev);
     if (rc == RCS_OK) ws->has_norm = true;
     return rc;
+}
+
+int adamw_clip_step_noalloc(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
+                            float lr, float wd, float clip, double *norm_out,
+                            hipStream_t stream) {
+    int rc;
+    if ((rc = validate_step(w, g, m, v, n, t, lr, wd, clip, 1.0f)) != RCS_OK) return rc;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RCS_EHIP;
+    if (norm_out != nullptr && (rc = check_norm_out(norm_out, dev)) != RCS_OK) return rc;
+    // every valid n fits: the norm pass never has more than kNormMaxBlocks blocks
+    if ((size_t)norm_blocks(n) * sizeof(double) > kScratchRecordOffset) return RCS_ESIZE;
+    char *base = nullptr;
+    if ((rc = scratch_address(dev, &base)) != RCS_OK) return rc;
+    NormBuffers nb;
+    nb.partials = reinterpret_cast<double *>(base);
+    nb.scalars = reinterpret_cast<ClipScalars *>(base + kScratchRecordOffset);
+    if ((rc = launch_step(w, g, m, v, n, clip, host_scalars(t, lr, wd, 1.0f), &nb, stream,
+                          nullptr)) != RCS_OK)
+        return rc;
+    if (norm_out != nullptr &&
+        hipMemcpyAsync(norm_out, &nb.scalars->norm, sizeof(double), hipMemcpyDefault, stream) !=
+            hipSuccess)
+        return RCS_EHIP;
+    return RCS_OK;
 }
 
 int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream) {
