@@ -67,9 +67,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_adamw_clip_step.argtypes = [f32p, f32p, f32p, f32p, i64, i32, ctypes.c_float,
                                              ctypes.c_float, ctypes.c_float, f64p]
         L.oracle_adamw_clip_step.restype = ctypes.c_int
-        L.oracle_scalar_step_f64.argtypes = [f64p, ctypes.c_double, ctypes.c_double,
-                                             ctypes.c_double, ctypes.c_double]
-        L.oracle_scalar_step_f64.restype = None
+        L.oracle_adamw_clip_step_f64.argtypes = [f64p, f64p, f64p, f64p, i64, i32,
+                                                 ctypes.c_double, ctypes.c_double,
+                                                 ctypes.c_double, f64p]
+        L.oracle_adamw_clip_step_f64.restype = ctypes.c_int
         L.oracle_ckpt_bytes.argtypes = [i64]
         L.oracle_ckpt_bytes.restype = i64
         L.oracle_ckpt_pack.argtypes = [i32, i64, f32p, f32p, f32p, u8p, i64]
@@ -178,11 +179,23 @@ def adamw_clip_step_accum(w, g_sum, m, v, t: int, lr: float, wd: float, clip: fl
     return adamw_clip_step(w, g, m, v, t, lr, wd, clip)
 
 
-def scalar_step_f64(state, g: float, lr: float, wd: float, clip: float):
-    """The worked example's float64 scalar step; state = [theta, m, v, t]."""
-    st = (ctypes.c_double * 4)(*[float(x) for x in state])
-    lib().oracle_scalar_step_f64(st, g, lr, wd, clip)
-    return [st[0], st[1], st[2], int(st[3])]
+def _f64(a: np.ndarray, writable: bool = False):
+    if a.dtype != np.float64 or not a.flags.c_contiguous:
+        raise TypeError("expected a C-contiguous float64 array")
+    if writable and not a.flags.writeable:
+        raise TypeError("array must be writable")
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def adamw_clip_step_f64(w, g, m, v, t: int, lr: float, wd: float, clip: float):
+    """The clipped AdamW definition in float64 over float64 arrays, in place.
+    Returns (status, pre-clip norm)."""
+    n = w.size
+    assert g.size == n and m.size == n and v.size == n
+    norm = ctypes.c_double(0.0)
+    rc = lib().oracle_adamw_clip_step_f64(_f64(w, True), _f64(g), _f64(m, True), _f64(v, True),
+                                          n, t, lr, wd, clip, ctypes.byref(norm))
+    return rc, norm.value
 
 
 def ckpt_bytes(n: int) -> int:

@@ -171,23 +171,38 @@ int oracle_adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t
     return ORACLE_OK;
 }
 
-/* The worked example's scalar step of "Training as a Recoverable State
- * Transition", Example 1, in float64 with its hyper-parameters passed in:
- * per-scalar clip to |g| <= clip, t advanced first, then the AdamW rule.
- * state = {theta, m, v, t}. */
-void oracle_scalar_step_f64(double state[4], double g, double lr, double wd, double clip) {
-    double theta = state[0], m = state[1], v = state[2], t = state[3];
-    if (g != 0.0 && fabs(g) > clip) g = g * (clip / fabs(g));
-    t = t + 1.0;
-    m = 0.9 * m + 0.1 * g;
-    v = 0.999 * v + 0.001 * g * g;
-    double mh = m / (1.0 - pow(0.9, t));
-    double vh = v / (1.0 - pow(0.999, t));
-    theta = theta * (1.0 - lr * wd) - lr * mh / (sqrt(vh) + 1e-8);
-    state[0] = theta;
-    state[1] = m;
-    state[2] = v;
-    state[3] = t;
+/* The definition of the clipped AdamW update ("Training as a Recoverable State
+ * Transition", section "The Exact Targets of Clipping and AdamW") evaluated in
+ * float64 from start to end, over a vector: one global L2 clip of g to norm
+ * <= clip (no epsilon), then for the 1-based update index t the moving
+ * averages m = beta1 m + (1 - beta1) g' and v = beta2 v + (1 - beta2) g'^2,
+ * their bias corrections by 1 - beta^t, and every parameter decayed by
+ * (1 - lr wd) before the Adam step lr m_hat / (sqrt(v_hat) + eps) is taken
+ * off it. The page's worked example (Example 1) prints float64 figures; this
+ * function is what they pin, and it in turn bounds the float32 sequence
+ * above. ORACLE_SKIPPED (w, m, v untouched) for a non-finite norm. */
+int oracle_adamw_clip_step_f64(double *w, const double *g, double *m, double *v, int64_t n,
+                               int32_t t, double lr, double wd, double clip, double *norm_out) {
+    const double beta1 = 0.9, beta2 = 0.999, eps = 1e-8;
+    if (!w || !g || !m || !v || n <= 0 || t < 1 || !(clip > 0.0)) return ORACLE_EINVAL;
+    double sumsq = 0.0;
+    for (int64_t i = 0; i < n; ++i) sumsq += g[i] * g[i];
+    const double norm = sqrt(sumsq);
+    if (norm_out) *norm_out = norm;
+    if (!isfinite(norm)) return ORACLE_SKIPPED;
+    const double scale = (norm > clip) ? clip / norm : 1.0;
+    const double corr1 = 1.0 - pow(beta1, (double)t);
+    const double corr2 = 1.0 - pow(beta2, (double)t);
+    const double keep = 1.0 - lr * wd;
+    for (int64_t i = 0; i < n; ++i) {
+        const double gi = g[i] * scale;
+        m[i] = beta1 * m[i] + (1.0 - beta1) * gi;
+        v[i] = beta2 * v[i] + (1.0 - beta2) * (gi * gi);
+        const double m_hat = m[i] / corr1;
+        const double v_hat = v[i] / corr2;
+        w[i] = keep * w[i] - lr * m_hat / (sqrt(v_hat) + eps);
+    }
+    return ORACLE_OK;
 }
 
 /* ---- state layout ---- */

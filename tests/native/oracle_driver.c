@@ -16,7 +16,8 @@ void oracle_adamw_elems(float *w, const float *g, float *m, float *v, int64_t n,
 void oracle_scale_grads(float *g, int64_t n, float scale);
 int oracle_adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                            float lr, float wd, float clip, double *norm_out);
-void oracle_scalar_step_f64(double state[4], double g, double lr, double wd, double clip);
+int oracle_adamw_clip_step_f64(double *w, const double *g, double *m, double *v, int64_t n,
+                               int32_t t, double lr, double wd, double clip, double *norm_out);
 int64_t oracle_ckpt_bytes(int64_t n);
 int oracle_ckpt_pack(int32_t step, int64_t n, const float *w, const float *m, const float *v,
                      uint8_t *buf, int64_t len);
@@ -52,9 +53,9 @@ int main(void) {
     oracle_scalars(2, 3e-3f, 0.01f, &bc1, &bc2, &decay);
     oracle_adamw_elems(w, g, m, v, N, oracle_clip_scale(norm, 1.0f), bc1, bc2, decay, 3e-3f);
     oracle_scale_grads(g, N, 0.5f);
-    double s4[4] = {2.0, 0.0, 0.0, 0.0};
-    oracle_scalar_step_f64(s4, 0.5, 0.1, 0.01, 1.0);
-    EXPECT(fabs(s4[0] - 1.898) < 1e-7);
+    double w64 = 2.0, g64 = 0.5, m64 = 0.0, v64 = 0.0, n64 = 0.0;
+    EXPECT(oracle_adamw_clip_step_f64(&w64, &g64, &m64, &v64, 1, 1, 0.1, 0.01, 1.0, &n64) == 0);
+    EXPECT(fabs(w64 - 1.898) < 1e-7 && n64 == 0.5);
     const int64_t len = oracle_ckpt_bytes(N);
     uint8_t *buf = malloc((size_t)len);
     EXPECT(oracle_ckpt_pack(7, N, w, m, v, buf, len) == 0);

@@ -36,35 +36,69 @@ def test_subnormals_kept_in_process():
     assert oracle.subnormals_kept()
 
 
-def test_worked_example_float64_scalar_step():
+def _f64(*xs):
+    return np.array(xs, dtype=np.float64)
+
+
+def test_worked_example_float64_definition():
+    """The update's definition in float64 on the one-dimensional example:
+    the moments, their bias-corrected values, the decayed weight and the
+    weight after the step printed on the page."""
     ex = _golden("worked_example_1d.json")
     inp, s1 = ex["inputs"], ex["step1"]
-    st = oracle.scalar_step_f64([inp["theta0"], 0.0, 0.0, 0], inp["grads"][0], inp["lr"],
-                                inp["wd"], inp["clip"])
-    assert abs(st[0] - s1["theta"]) < s1["theta_abs_tol"]
-    assert st[1] == pytest.approx(s1["m"], rel=1e-15)
-    assert st[2] == pytest.approx(s1["v"], rel=1e-15)
-    assert st[3] == 1
-    # bias-corrected moments printed on the page
-    assert st[1] / (1 - 0.9) == pytest.approx(s1["m_hat"], rel=1e-14)
-    assert st[2] / (1 - 0.999) == pytest.approx(s1["v_hat"], rel=1e-12)
+    w, g, m, v = _f64(inp["theta0"]), _f64(inp["grads"][0]), _f64(0), _f64(0)
+    rc, norm = oracle.adamw_clip_step_f64(w, g, m, v, 1, inp["lr"], inp["wd"], inp["clip"])
+    assert rc == oracle.OK and norm == abs(inp["grads"][0])  # below the threshold: no clip
+    assert abs(w[0] - s1["theta"]) < s1["theta_abs_tol"]
+    # (1 - beta) is formed in float64, a few ulps off the decimal figures
+    assert m[0] == pytest.approx(s1["m"], rel=4e-15)
+    assert v[0] == pytest.approx(s1["v"], rel=4e-15)
+    assert m[0] / (1 - 0.9) == pytest.approx(s1["m_hat"], rel=1e-14)
+    assert v[0] / (1 - 0.999) == pytest.approx(s1["v_hat"], rel=1e-12)
+    # the decayed weight: the step is lr * m_hat / sqrt(v_hat) = 0.1 off it
+    assert inp["theta0"] * (1 - inp["lr"] * inp["wd"]) == pytest.approx(s1["decayed_theta"])
+    assert s1["decayed_theta"] - w[0] == pytest.approx(s1["adaptive_step"], abs=1e-7)
 
 
-def test_worked_example_float64_resume():
-    ex = _golden("worked_example_1d.json")
-    inp = ex["inputs"]
-    args = (inp["lr"], inp["wd"], inp["clip"])
-    state = [inp["theta0"], 0.0, 0.0, 0]
-    cont = state
-    for g in inp["grads"]:
-        cont = oracle.scalar_step_f64(cont, g, *args)
-    prefix = state
-    for g in inp["grads"][:2]:
-        prefix = oracle.scalar_step_f64(prefix, g, *args)
-    resumed = oracle.scalar_step_f64(json.loads(json.dumps(prefix)), inp["grads"][2], *args)
-    assert cont == resumed
-    wrong = oracle.scalar_step_f64([prefix[0], 0.0, 0.0, 0], inp["grads"][2], *args)
-    assert abs(wrong[0] - cont[0]) > ex["resume"]["weights_only_resume_min_abs_diff"]
+def test_float64_definition_clips_the_whole_vector():
+    """g = (3, 4) has norm 5; with clip 1 the whole vector is scaled by 1/5
+    (direction kept), so at t = 1 m = 0.1 * (0.6, 0.8) and v = 0.001 * g'^2."""
+    w, g, m, v = _f64(1.0, -1.0), _f64(3.0, 4.0), _f64(0, 0), _f64(0, 0)
+    rc, norm = oracle.adamw_clip_step_f64(w, g, m, v, 1, 0.01, 0.0, 1.0)
+    assert rc == oracle.OK and norm == 5.0
+    assert m == pytest.approx([0.06, 0.08], rel=1e-14)
+    assert v == pytest.approx([0.001 * 0.36, 0.001 * 0.64], rel=1e-13)
+    # m_hat = g', v_hat = g'^2: each weight moves by lr * |g'| / (|g'| + eps) ~ lr
+    assert w == pytest.approx([1.0 - 0.01, -1.0 - 0.01], abs=1e-9)
+    g[1] = np.inf
+    assert oracle.adamw_clip_step_f64(w, g, m, v, 2, 0.01, 0.0, 1.0)[0] == oracle.SKIPPED
+
+
+def test_float64_definition_resume_needs_the_whole_state():
+    """Six updates of a seven-element vector straight through equal three, a
+    round trip of (w, m, v) through their bytes, and three more from t = 4;
+    restarting with the weights only (m = v = 0, t from 1) does not."""
+    rng = np.random.default_rng(11)
+    w0 = rng.standard_normal(7)
+    gs = [rng.standard_normal(7) * 0.3 for _ in range(6)]
+    hp = (0.05, 0.01, 1.0)
+    w, m, v = w0.copy(), np.zeros(7), np.zeros(7)
+    for t, g in enumerate(gs, start=1):
+        oracle.adamw_clip_step_f64(w, g, m, v, t, *hp)
+    w2, m2, v2 = w0.copy(), np.zeros(7), np.zeros(7)
+    for t, g in enumerate(gs[:3], start=1):
+        oracle.adamw_clip_step_f64(w2, g, m2, v2, t, *hp)
+    blob = w2.tobytes() + m2.tobytes() + v2.tobytes()
+    w3, m3, v3 = (np.frombuffer(blob[k * 56:(k + 1) * 56], dtype=np.float64).copy()
+                  for k in range(3))
+    for t, g in enumerate(gs[3:], start=4):
+        oracle.adamw_clip_step_f64(w3, g, m3, v3, t, *hp)
+    assert w3.tobytes() == w.tobytes() and m3.tobytes() == m.tobytes()
+    assert v3.tobytes() == v.tobytes()
+    w4, m4, v4 = w2.copy(), np.zeros(7), np.zeros(7)
+    for t, g in enumerate(gs[3:], start=1):
+        oracle.adamw_clip_step_f64(w4, g, m4, v4, t, *hp)
+    assert np.abs(w4 - w).max() > 1e-3
 
 
 def _vec(x):
@@ -107,13 +141,13 @@ def test_worked_example_float32_three_steps_and_resume():
     assert rc == oracle.OK and step == 2
     oracle.adamw_clip_step(w3, _vec(inp["grads"][2]), m3, v3, step + 1, *hp)
     assert f32bits(w3) == f32bits(w) and f32bits(m3) == f32bits(m) and f32bits(v3) == f32bits(v)
-    # float32 sequence tracks the page's float64 program within a few float32 ulps
-    st = [inp["theta0"], 0.0, 0.0, 0]
-    for g in inp["grads"]:
-        st = oracle.scalar_step_f64(st, g, *hp)
-    assert abs(float(w[0]) - st[0]) <= 4 * np.spacing(np.float32(st[0]))
-    assert abs(float(m[0]) - st[1]) <= 4 * np.spacing(np.float32(st[1]))
-    assert abs(float(v[0]) - st[2]) <= 4 * np.spacing(np.float32(st[2]))
+    # the float32 sequence tracks the float64 definition within a few float32 ulps
+    w64, m64, v64 = _f64(inp["theta0"]), _f64(0), _f64(0)
+    for t, g in enumerate(inp["grads"], start=1):
+        oracle.adamw_clip_step_f64(w64, _f64(g), m64, v64, t, *hp)
+    assert abs(float(w[0]) - w64[0]) <= 4 * np.spacing(np.float32(w64[0]))
+    assert abs(float(m[0]) - m64[0]) <= 4 * np.spacing(np.float32(m64[0]))
+    assert abs(float(v[0]) - v64[0]) <= 4 * np.spacing(np.float32(v64[0]))
     # weights-only resume (m = v = 0, t restarts) diverges
     ww, mm, vv = w2.copy(), _vec(0), _vec(0)
     oracle.adamw_clip_step(ww, _vec(inp["grads"][2]), mm, vv, 1, *hp)

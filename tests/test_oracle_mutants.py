@@ -86,10 +86,19 @@ MUTANTS = [
     ("unpack swaps m and v",
      "m[i] = get_f32_le(pm + 4 * i);\n        v[i] = get_f32_le(pv + 4 * i);",
      "m[i] = get_f32_le(pv + 4 * i);\n        v[i] = get_f32_le(pm + 4 * i);"),
-    ("worked example: t advanced after the bias correction",
-     "    t = t + 1.0;\n    m = 0.9 * m + 0.1 * g;", "    m = 0.9 * m + 0.1 * g;"),
-    ("worked example: square dropped",
-     "v = 0.999 * v + 0.001 * g * g;", "v = 0.999 * v + 0.001 * g;"),
+    ("float64 definition: square dropped",
+     "v[i] = beta2 * v[i] + (1.0 - beta2) * (gi * gi);", "v[i] = beta2 * v[i] + (1.0 - beta2) * gi;"),
+    ("float64 definition: bias correction with t + 1",
+     "const double corr1 = 1.0 - pow(beta1, (double)t);",
+     "const double corr1 = 1.0 - pow(beta1, (double)t + 1.0);"),
+    ("float64 definition: decay applied after the step",
+     "w[i] = keep * w[i] - lr * m_hat / (sqrt(v_hat) + eps);",
+     "w[i] = keep * (w[i] - lr * m_hat / (sqrt(v_hat) + eps));"),
+    ("float64 definition: clip factor inverted",
+     "const double scale = (norm > clip) ? clip / norm : 1.0;",
+     "const double scale = (norm > clip) ? norm / clip : 1.0;"),
+    ("float64 definition: moments not carried between updates",
+     "m[i] = beta1 * m[i] + (1.0 - beta1) * gi;", "m[i] = (1.0 - beta1) * gi;"),
 ]
 
 
