@@ -5,15 +5,24 @@ modes the schema must guard against).
 Each rank owns a contiguous slice [param_shard_offset, + param_shard_numel) of
 the flat parameter vector and writes its slice of (w, m, v) as its own step
 file (the same [int32 step][int32 n][w][m][v] layout, n = the slice's size)
-through the library's atomic write; the manifest is written last, also
-atomically, so a crash never leaves a manifest that points at partial shards.
-On one GPU the ranks are simulated in one process, as the lesson's own test
-does; each rank's pack is the library's ckpt_pack of its slice.
+through the library's atomic write (temporary file, fsync, rename, fsync of
+the directory). Shard files are named for the step and for the save
+(step_NNNNNN.rank{r}.{token}.bin), so a save never overwrites a file the
+current manifest names; the new manifest is renamed into place only after
+every shard is on disk, which is the single commit point, and only then are
+the previous checkpoint's shard files removed. A crash anywhere during a save
+leaves the previous checkpoint loadable.
 
-Loading refuses, loudly: a world size other than the expected one, a shard
-count that differs from the world size, shards that do not tile [0, n), and a
-shard whose bytes do not hash to the manifest's sha256 (partial or corrupted
-write).
+One pinned staging buffer, sized to the largest shard, is made when a
+ShardedCheckpointer is created and reused for every rank and every save and
+load (the engine of the pages preallocates its buffers at start-up). On one
+GPU the ranks are simulated in one process, as the lesson's own test does;
+each rank's pack is the library's ckpt_pack of its slice.
+
+Loading refuses, loudly and before any device memory is written: a world
+size other than the expected one, a shard count that differs from the world
+size, shards that do not tile [0, n), and a shard whose bytes do not hash to
+the manifest's sha256 (partial or corrupted write).
 
 The file layer is host-side orchestration around the C ABI (sha256 from
 hashlib); all device work is the library's pack/unpack.
@@ -25,6 +34,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import re
 
 import numpy as np
 import torch
@@ -92,32 +102,8 @@ def _write_atomic(path: str, data: bytes) -> None:
     _check(lib().rcs_file_write_atomic(_b(path), buf, len(data)), "rcs_file_write_atomic")
 
 
-def save_sharded(directory, step: int, w, m, v, world_size: int,
-                 wall_clock_seconds: float = 0.0, stream=None) -> ShardManifest:
-    """Writes rank{r}.bin for every simulated rank, then manifest.json."""
-    os.makedirs(directory, exist_ok=True)
-    n = w.numel()
-    shards = []
-    for r, (off, numel) in enumerate(shard_ranges(n, world_size)):
-        buf = torch.empty(ckpt_bytes(numel), dtype=torch.uint8, pin_memory=True)
-        ckpt_pack(step, w[off:off + numel], m[off:off + numel], v[off:off + numel], buf,
-                  stream=stream)
-        torch.cuda.synchronize()
-        name = f"rank{r}.bin"
-        _check(lib().ckpt_file_write_path(_b(os.path.join(directory, name)),
-                                          _host_u8(buf, "buf"), buf.numel()),
-               "ckpt_file_write_path")
-        digest = hashlib.sha256(buf.numpy()).hexdigest()
-        shards.append(ShardEntry(r, name, digest, off, numel))
-        del buf
-    man = ShardManifest(world_size, int(step), float(wall_clock_seconds), shards)
-    _write_atomic(os.path.join(directory, MANIFEST), man.to_json().encode())
-    return man
-
-
-def verify_sharded(directory, expected_world_size: int, n: int):
-    """Reads and checks the manifest and every shard; returns (manifest, list
-    of host byte buffers in rank order). Host-only: no device is touched."""
+def _read_manifest(directory, expected_world_size: int, n: int) -> ShardManifest:
+    """The manifest with every check that needs no shard bytes."""
     path = os.path.join(directory, MANIFEST)
     if not os.path.exists(path):
         raise ShardError(f"no manifest in {directory} (checkpoint incomplete)")
@@ -131,46 +117,138 @@ def verify_sharded(directory, expected_world_size: int, n: int):
     if len(man.shards) != man.world_size:
         raise ShardError(f"manifest lists {len(man.shards)} shards for "
                          f"world_size={man.world_size}")
-    shards = sorted(man.shards, key=lambda s: s.rank)
-    if [s.rank for s in shards] != list(range(man.world_size)):
+    man.shards = sorted(man.shards, key=lambda s: s.rank)
+    if [s.rank for s in man.shards] != list(range(man.world_size)):
         raise ShardError("shard ranks are not 0..world_size-1")
     off = 0
-    for s in shards:
+    for s in man.shards:
         if s.param_shard_offset != off or s.param_shard_numel <= 0:
             raise ShardError(f"rank {s.rank}: shards do not tile the parameter vector")
         off += s.param_shard_numel
-    if off != n:
-        raise ShardError(f"shards cover {off} parameters, expected {n}")
-    bufs = []
-    for s in shards:
         if os.path.basename(s.path) != s.path or s.path in ("", ".", ".."):
             raise ShardError(f"rank {s.rank}: shard path {s.path!r} is not a plain file name")
-        fpath = os.path.join(directory, s.path)
-        if not os.path.exists(fpath):
-            raise ShardError(f"rank {s.rank}: missing shard file {s.path}")
-        with open(fpath, "rb") as f:
-            raw = f.read()
-        if hashlib.sha256(raw).hexdigest() != s.sha256:
-            raise ShardError(f"rank {s.rank}: sha256 mismatch (partial or corrupted write)")
-        if len(raw) != ckpt_bytes(s.param_shard_numel):
-            raise ShardError(f"rank {s.rank}: {len(raw)} bytes for {s.param_shard_numel} params")
-        h_step = int.from_bytes(raw[0:4], "little", signed=True)
-        h_n = int.from_bytes(raw[4:8], "little", signed=True)
-        if h_step != man.step or h_n != s.param_shard_numel:
-            raise ShardError(f"rank {s.rank}: header (step {h_step}, n {h_n}) disagrees with "
-                             f"the manifest (step {man.step}, n {s.param_shard_numel})")
-        bufs.append(raw)
-    return man, bufs
+    if off != n:
+        raise ShardError(f"shards cover {off} parameters, expected {n}")
+    return man
+
+
+def _read_shard(directory, man: ShardManifest, s: ShardEntry, out: np.ndarray) -> np.ndarray:
+    """Reads shard s into out[:size] and checks its size, sha256 and header
+    against the manifest; returns the filled view."""
+    fpath = os.path.join(directory, s.path)
+    if not os.path.exists(fpath):
+        raise ShardError(f"rank {s.rank}: missing shard file {s.path}")
+    size = os.path.getsize(fpath)
+    want = ckpt_bytes(s.param_shard_numel)
+    if size != want:
+        raise ShardError(f"rank {s.rank}: {size} bytes for {s.param_shard_numel} params")
+    if size > out.size:
+        raise ShardError(f"rank {s.rank}: {size} bytes exceed the {out.size}-byte staging buffer")
+    view = out[:size]
+    with open(fpath, "rb", buffering=0) as f:
+        got = f.readinto(memoryview(view))
+    if got != size:
+        raise ShardError(f"rank {s.rank}: short read of {s.path}")
+    if hashlib.sha256(view).hexdigest() != s.sha256:
+        raise ShardError(f"rank {s.rank}: sha256 mismatch (partial or corrupted write)")
+    h_step = int.from_bytes(view[0:4].tobytes(), "little", signed=True)
+    h_n = int.from_bytes(view[4:8].tobytes(), "little", signed=True)
+    if h_step != man.step or h_n != s.param_shard_numel:
+        raise ShardError(f"rank {s.rank}: header (step {h_step}, n {h_n}) disagrees with "
+                         f"the manifest (step {man.step}, n {s.param_shard_numel})")
+    return view
+
+
+def verify_sharded(directory, expected_world_size: int, n: int,
+                   staging: np.ndarray | None = None) -> ShardManifest:
+    """Checks the manifest and every shard (size, sha256, header); returns the
+    manifest. Host-only: no device is touched. staging: a uint8 buffer at
+    least as large as the largest shard (one is made if absent)."""
+    man = _read_manifest(directory, expected_world_size, n)
+    if staging is None:
+        staging = np.empty(max(ckpt_bytes(s.param_shard_numel) for s in man.shards), np.uint8)
+    for s in man.shards:
+        _read_shard(directory, man, s, staging)
+    return man
+
+
+class ShardedCheckpointer:
+    """Sharded save and load of (w, m, v) over float32[n] for a fixed world
+    size, through one pinned staging buffer made here and reused."""
+
+    def __init__(self, directory, n: int, world_size: int):
+        self.dir, self.n, self.world_size = str(directory), int(n), int(world_size)
+        self.ranges = shard_ranges(self.n, self.world_size)
+        largest = max(ckpt_bytes(k) for _, k in self.ranges)
+        self.staging = torch.empty(largest, dtype=torch.uint8, pin_memory=True)
+        os.makedirs(self.dir, exist_ok=True)
+
+    def save(self, step: int, w, m, v, wall_clock_seconds: float = 0.0,
+             stream=None) -> ShardManifest:
+        """Writes every rank's shard under a name of this save, then the
+        manifest (the commit), then removes shard files the manifest does not
+        name."""
+        if w.numel() != self.n:
+            raise ValueError(f"w has {w.numel()} elements, the checkpointer {self.n}")
+        token = os.urandom(4).hex()
+        shards = []
+        for r, (off, numel) in enumerate(self.ranges):
+            buf = self.staging[:ckpt_bytes(numel)]
+            ckpt_pack(step, w[off:off + numel], m[off:off + numel], v[off:off + numel], buf,
+                      stream=stream)
+            torch.cuda.synchronize()
+            name = f"step_{int(step):06d}.rank{r}.{token}.bin"
+            _check(lib().ckpt_file_write_path(_b(os.path.join(self.dir, name)),
+                                              _host_u8(buf, "buf"), buf.numel()),
+                   "ckpt_file_write_path")
+            shards.append(ShardEntry(r, name, hashlib.sha256(buf.numpy()).hexdigest(), off,
+                                     numel))
+        man = ShardManifest(self.world_size, int(step), float(wall_clock_seconds), shards)
+        _write_atomic(os.path.join(self.dir, MANIFEST), man.to_json().encode())
+        keep = {s.path for s in shards}
+        for f in os.listdir(self.dir):
+            if SHARD_FILE.fullmatch(f) and f not in keep:
+                try:
+                    os.remove(os.path.join(self.dir, f))
+                except FileNotFoundError:
+                    pass
+        return man
+
+    def load(self, w, m, v, stream=None) -> int:
+        """Verifies every shard first (nothing is written to the device if any
+        check fails), then reads each again, checks its hash again and unpacks
+        it into its slice of w, m, v; returns the step (continue with
+        t = step + 1)."""
+        if w.numel() != self.n:
+            raise ValueError(f"w has {w.numel()} elements, the checkpointer {self.n}")
+        man = _read_manifest(self.dir, self.world_size, self.n)
+        need = max(ckpt_bytes(s.param_shard_numel) for s in man.shards)
+        if need > self.staging.numel():  # a checkpoint split differently from this one
+            self.staging = torch.empty(need, dtype=torch.uint8, pin_memory=True)
+        host = self.staging.numpy()
+        for s in man.shards:
+            _read_shard(self.dir, man, s, host)
+        for s in man.shards:
+            view = _read_shard(self.dir, man, s, host)
+            a, k = s.param_shard_offset, s.param_shard_numel
+            ckpt_unpack(self.staging[:view.size], w[a:a + k], m[a:a + k], v[a:a + k],
+                        stream=stream)
+            torch.cuda.synchronize()
+        return man.step
+
+
+# Shard files a save writes (and removes once a newer manifest is in place),
+# with the atomic write's temporaries.
+SHARD_FILE = re.compile(r"step_\d+\.rank\d+\.[0-9a-f]+\.bin(\.tmp)?")
+
+
+def save_sharded(directory, step: int, w, m, v, world_size: int,
+                 wall_clock_seconds: float = 0.0, stream=None) -> ShardManifest:
+    """One save through a ShardedCheckpointer made for it."""
+    return ShardedCheckpointer(directory, w.numel(), world_size).save(
+        step, w, m, v, wall_clock_seconds, stream)
 
 
 def load_sharded(directory, expected_world_size: int, w, m, v, stream=None) -> int:
-    """Verifies everything first, then unpacks each shard into its slice of
-    w, m, v; returns the step (continue with t = step + 1)."""
-    man, bufs = verify_sharded(directory, expected_world_size, w.numel())
-    for s, raw in zip(sorted(man.shards, key=lambda e: e.rank), bufs):
-        host = torch.empty(len(raw), dtype=torch.uint8, pin_memory=True)
-        host.numpy()[:] = np.frombuffer(raw, dtype=np.uint8)
-        a, k = s.param_shard_offset, s.param_shard_numel
-        ckpt_unpack(host, w[a:a + k], m[a:a + k], v[a:a + k], stream=stream)
-        torch.cuda.synchronize()
-    return man.step
+    """One load through a ShardedCheckpointer made for it."""
+    return ShardedCheckpointer(directory, w.numel(), expected_world_size).load(w, m, v, stream)

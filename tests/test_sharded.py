@@ -56,8 +56,9 @@ def test_shard_ranges_tile_and_align():
 def test_verify_accepts_consistent_checkpoint(tmp_path):
     w, m, v = _arrays(1000)
     _write_host_sharded(tmp_path, 1234, w, m, v, 4)
-    man, bufs = sharded.verify_sharded(tmp_path, 4, 1000)
-    assert man.step == 1234 and man.world_size == 4 and len(bufs) == 4
+    man = sharded.verify_sharded(tmp_path, 4, 1000)
+    assert man.step == 1234 and man.world_size == 4 and len(man.shards) == 4
+    bufs = [open(tmp_path / s.path, "rb").read() for s in man.shards]
     joined = np.concatenate([np.frombuffer(b[8:8 + 4 * s.param_shard_numel], np.float32)
                              for b, s in zip(bufs, man.shards)])
     assert (joined.view(np.uint32) == w.view(np.uint32)).all()
@@ -147,7 +148,8 @@ def test_gpu_save_load_round_trip_matches_oracle_shards(tmp_path, world):
     dw, dm, dv = (torch.from_numpy(a).cuda() for a in (w, m, v))
     man = sharded.save_sharded(tmp_path, 80, dw, dm, dv, world, wall_clock_seconds=3.0)
     assert sorted(os.listdir(tmp_path)) == sorted(["manifest.json"] +
-                                                  [f"rank{r}.bin" for r in range(world)])
+                                                  [s.path for s in man.shards])
+    assert all(s.path.startswith(f"step_000080.rank{s.rank}.") for s in man.shards)
     for s in man.shards:  # every shard file is the oracle's pack of that slice
         a, k = s.param_shard_offset, s.param_shard_numel
         _, ob = oracle.ckpt_pack(80, w[a:a + k].copy(), m[a:a + k].copy(), v[a:a + k].copy())
@@ -158,3 +160,74 @@ def test_gpu_save_load_round_trip_matches_oracle_shards(tmp_path, world):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     with pytest.raises(sharded.ShardError):
         sharded.load_sharded(tmp_path, world + 1, *out)
+
+
+def _fake_ckpt(monkeypatch, fail_after_rank=None):
+    """Routes the checkpointer's device pack through the oracle's pack of host
+    arrays (no GPU), and can make the shard write fail after a given rank,
+    as a crash in the middle of a save would."""
+    def pack(step, w, m, v, buf, stream=None):
+        _, ob = oracle.ckpt_pack(step, w.numpy().copy(), m.numpy().copy(), v.numpy().copy())
+        buf.numpy()[:] = ob
+        return buf
+
+    monkeypatch.setattr(sharded, "ckpt_pack", pack)
+    monkeypatch.setattr(sharded.torch.cuda, "synchronize", lambda *a, **k: None)
+    real = rcs.lib().ckpt_file_write_path
+    calls = {"n": 0}
+
+    class Lib:
+        def __getattr__(self, name):
+            return getattr(rcs.lib(), name)
+
+        def ckpt_file_write_path(self, path, buf, nbytes):
+            if fail_after_rank is not None and calls["n"] > fail_after_rank:
+                raise KeyboardInterrupt("simulated crash")
+            calls["n"] += 1
+            return real(path, buf, nbytes)
+
+    monkeypatch.setattr(sharded, "lib", lambda: Lib())
+    monkeypatch.setattr(sharded.torch, "empty",
+                        lambda k, dtype=None, pin_memory=False: torch.zeros(k, dtype=dtype))
+
+
+def test_crash_during_a_save_keeps_the_previous_checkpoint(tmp_path, monkeypatch):
+    """Save at step 80, then a save at step 160 that dies after rewriting
+    rank 0 (and again after rank 2): the step-80 manifest and shards are
+    untouched, verify and the shard bytes still give step 80."""
+    n, world = 4000, 4
+    w, m, v = (torch.from_numpy(a) for a in _arrays(n, seed=5))
+    _fake_ckpt(monkeypatch)
+    ck = sharded.ShardedCheckpointer(tmp_path, n, world)
+    man80 = ck.save(80, w, m, v)
+    before = {f: open(tmp_path / f, "rb").read() for f in os.listdir(tmp_path)}
+    for fail_after in (0, 2):
+        _fake_ckpt(monkeypatch, fail_after_rank=fail_after)
+        ck = sharded.ShardedCheckpointer(tmp_path, n, world)
+        with pytest.raises(KeyboardInterrupt):
+            ck.save(160, w * 2, m * 2, v * 2)
+        man = sharded.verify_sharded(tmp_path, world, n)
+        assert man.step == 80 and [s.path for s in man.shards] == [s.path for s in man80.shards]
+        for f, data in before.items():
+            assert open(tmp_path / f, "rb").read() == data
+    # a completed save then replaces it and removes the step-80 shards
+    _fake_ckpt(monkeypatch)
+    man160 = sharded.ShardedCheckpointer(tmp_path, n, world).save(160, w * 2, m * 2, v * 2)
+    assert sharded.verify_sharded(tmp_path, world, n).step == 160
+    left = sorted(os.listdir(tmp_path))
+    assert left == sorted(["manifest.json"] + [s.path for s in man160.shards])
+
+
+def test_checkpointer_reuses_one_staging_buffer(tmp_path, monkeypatch):
+    """Every rank of every save goes through the buffer made at construction,
+    sized to the largest shard."""
+    n, world = 4003, 4
+    w, m, v = (torch.from_numpy(a) for a in _arrays(n, seed=6))
+    _fake_ckpt(monkeypatch)
+    ck = sharded.ShardedCheckpointer(tmp_path, n, world)
+    staging = ck.staging
+    assert staging.numel() == max(rcs.ckpt_bytes(k) for _, k in sharded.shard_ranges(n, world))
+    for step in (1, 2, 3):
+        ck.save(step, w, m, v)
+        assert ck.staging is staging
+    assert sharded.verify_sharded(tmp_path, world, n).step == 3
