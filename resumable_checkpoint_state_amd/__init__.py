@@ -342,8 +342,9 @@ def signals_poll() -> int:
 
 class CkptWriter:
     """The library's asynchronous step-file writer (rcs_ckpt_writer_*): it owns
-    a device snapshot, a pinned host buffer, a copy stream and a worker thread
-    that writes <dir>/step_NNNNNN.bin atomically and keeps the newest `keep`."""
+    a device snapshot, two pinned host images, a copy stream and a worker
+    thread that writes <dir>/step_NNNNNN.bin atomically and keeps the newest
+    `keep`."""
 
     def __init__(self, directory, n: int, keep: int = 3):
         os.makedirs(directory, exist_ok=True)
@@ -354,7 +355,8 @@ class CkptWriter:
 
     def submit(self, step: int, w, m, v, stream=None) -> None:
         """Snapshot of (w, m, v) on the stream, then copy and write in the
-        background; raises first if the previous write failed."""
+        background; waits only while the host image it reuses is still being
+        written; raises first if an earlier write failed."""
         if self._h is None:
             raise ValueError("writer is closed")
         n = self.n
@@ -363,8 +365,8 @@ class CkptWriter:
                "rcs_ckpt_writer_submit")
 
     def wait(self) -> str:
-        """Waits for the write in flight; returns the path written since the
-        last wait ("" if none) or raises its error."""
+        """Waits for the writes in flight; returns the newest path written
+        since the last wait ("" if none) or raises a failure."""
         if self._h is None:
             return ""
         out = ctypes.create_string_buffer(4096)
@@ -394,15 +396,17 @@ class StepFileCheckpointer:
     async_write=True hands each save to the library's CkptWriter (a device
     snapshot on the training stream, the copy on its own stream, the atomic
     write and rotation on its worker thread), so training continues during
-    both the host-link copy and the disk write; the next save, a SIGTERM save
-    and flush() wait for the previous write first."""
+    both the host-link copy and the disk write; a save waits only while the
+    writer's host image it reuses is still being written (two saves back). A
+    SIGTERM save and flush() wait for every write in flight; a failed write
+    raises from a later save or from flush()."""
 
     def __init__(self, directory, n: int, every: int = 100, keep: int = 3,
                  install_signals: bool = True, stream=None, async_write: bool = False):
         self.dir, self.n, self.every, self.keep = directory, int(n), int(every), int(keep)
         os.makedirs(directory, exist_ok=True)
         self.stream = stream
-        self.written: list[str] = []
+        self.written: list[str] = []  # files saved (asynchronous ones once submitted)
         self.async_write = bool(async_write)
         self._buf: torch.Tensor | None = None  # pinned host image, made on first use
         self._writer = CkptWriter(directory, self.n, self.keep) if self.async_write else None
@@ -418,11 +422,9 @@ class StepFileCheckpointer:
         return self._buf
 
     def flush(self) -> None:
-        """Waits for an asynchronous write in flight and raises its error."""
+        """Waits for the asynchronous writes in flight and raises a failure."""
         if self._writer is not None:
-            path = self._writer.wait()
-            if path:
-                self.written.append(path)
+            self._writer.wait()
 
     def close(self) -> None:
         """flush(), then frees the asynchronous writer."""
@@ -433,7 +435,6 @@ class StepFileCheckpointer:
             self.async_write = False
 
     def save(self, t: int, w, m, v, wait: bool = False) -> None:
-        self.flush()
         if self._writer is None:
             ckpt_pack(t, w, m, v, self.buf, stream=self.stream)
             torch.cuda.synchronize()
@@ -441,6 +442,7 @@ class StepFileCheckpointer:
             ckpt_file_rotate(self.dir, self.keep)
             return
         self._writer.submit(t, w, m, v, stream=self.stream)
+        self.written.append(os.path.join(os.fspath(self.dir), step_file_name(t)))
         if wait:
             self.flush()
 

@@ -2,8 +2,10 @@
 // writer's worker thread, its mutex and condition variable, and concurrent
 // submit / wait calls, with the device side replaced by plain host stand-ins
 // (no GPU, no HIP runtime linked). The stand-ins keep the contract the writer
-// relies on: ckpt_pack_async takes the state at the call and lands it in the
-// host buffer later, on another thread; ckpt_pack_wait blocks until it has.
+// relies on: ckpt_pack_async takes the state at the call (after the previous
+// copy out of the same snapshot has landed, as the library orders its snapshot
+// kernel on the device) and lands it in the host buffer later, on another
+// thread; ckpt_pack_wait blocks until the newest such copy has landed.
 // The file side is the real csrc/ckpt_io.cpp.
 //
 // usage: writer_tsan_driver DIR     prints "writer tsan driver ok" on success
@@ -11,10 +13,12 @@
 
 #include <atomic>
 #include <chrono>
+#include <condition_variable>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -51,8 +55,25 @@ hipError_t hipGetLastError(void) { return hipSuccess; }
 
 // ---------------------------------------------------------------- pack stand-ins
 namespace {
+// One "copy" out of a snapshot: a thread that lands the payload later, and a
+// flag set when it has.
+struct CopyDone {
+    std::mutex mu;
+    std::condition_variable cv;
+    bool done = false;
+};
+struct SnapState {
+    std::vector<std::thread> threads;
+    std::shared_ptr<CopyDone> last;  // the newest copy out of the snapshot
+};
 std::mutex g_mu;
-std::map<const void *, std::thread> g_copies;  // snapshot -> the "copy stream"
+std::map<const void *, SnapState> g_snaps;
+
+void wait_done(const std::shared_ptr<CopyDone> &d) {
+    if (!d) return;
+    std::unique_lock<std::mutex> lk(d->mu);
+    d->cv.wait(lk, [&] { return d->done; });
+}
 
 void put_le32(unsigned char *p, int32_t x) {
     const uint32_t u = (uint32_t)x;
@@ -61,12 +82,15 @@ void put_le32(unsigned char *p, int32_t x) {
 }  // namespace
 
 void rcs_snapshot_forget(int, const void *snapshot) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_copies.find(snapshot);
-    if (it != g_copies.end()) {
-        if (it->second.joinable()) it->second.join();
-        g_copies.erase(it);
+    std::vector<std::thread> ts;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_snaps.find(snapshot);
+        if (it == g_snaps.end()) return;
+        ts.swap(it->second.threads);
+        g_snaps.erase(it);
     }
+    for (auto &t : ts) t.join();
 }
 
 extern "C" {
@@ -77,6 +101,13 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
                     float *snapshot, int64_t snapshot_bytes, void *host_buf, int64_t buf_bytes,
                     hipStream_t, hipStream_t) {
     if (snapshot_bytes != 12 * n || buf_bytes != 8 + 12 * n) return RCS_ESIZE;
+    std::shared_ptr<CopyDone> prev;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        prev = g_snaps[snapshot].last;
+    }
+    // the library orders the snapshot kernel after the previous copy out of it
+    wait_done(prev);
     // the "snapshot kernel": the state at the call
     std::memcpy(snapshot, w, 4 * n);
     std::memcpy(snapshot + n, m, 4 * n);
@@ -85,26 +116,33 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
     put_le32(b, step);
     put_le32(b + 4, (int32_t)n);
     // the "copy stream": lands the payload a little later, on another thread
+    auto d = std::make_shared<CopyDone>();
     std::thread copy([=] {
         std::this_thread::sleep_for(std::chrono::milliseconds(2));
         std::memcpy(b + 8, snapshot, 12 * n);
+        {
+            std::lock_guard<std::mutex> lk(d->mu);
+            d->done = true;
+        }
+        d->cv.notify_all();
     });
     std::lock_guard<std::mutex> lk(g_mu);
-    auto &slot = g_copies[snapshot];
-    if (slot.joinable()) slot.join();  // the writer waits for the previous copy first
-    slot = std::move(copy);
+    SnapState &st = g_snaps[snapshot];
+    st.threads.push_back(std::move(copy));
+    st.last = d;
     return RCS_OK;
 }
 
+// Blocks until the newest copy out of the snapshot has landed.
 int ckpt_pack_wait(const float *snapshot) {
-    std::thread t;
+    std::shared_ptr<CopyDone> d;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        auto it = g_copies.find(snapshot);
-        if (it == g_copies.end() || !it->second.joinable()) return RCS_OK;
-        t = std::move(it->second);
+        auto it = g_snaps.find(snapshot);
+        if (it == g_snaps.end()) return RCS_OK;
+        d = it->second.last;
     }
-    t.join();
+    wait_done(d);
     return RCS_OK;
 }
 }

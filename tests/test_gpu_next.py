@@ -257,8 +257,16 @@ def test_native_writer_reports_a_failed_write(dev, tmp_path):
     assert wr.wait() == ""  # reported once
     wr.submit(2, w, m, v)  # fails in the background again ...
     with pytest.raises(rcs.RcsError) as e:
-        wr.submit(3, w, m, v)  # ... and the next submit reports it, submitting nothing
+        # ... and a later submit reports it, submitting nothing: at the latest the
+        # one that reuses step 2's host image, which waits for step 2's write
+        for step in (3, 4):
+            wr.submit(step, w, m, v)
     assert e.value.status == rcs.EIO
+    try:
+        wr.wait()  # step 3's write, if it went out, failed too
+    except rcs.RcsError as e3:
+        assert e3.status == rcs.EIO
+    assert wr.wait() == ""
     os.makedirs(d)
     wr.submit(4, w, m, v)
     assert os.path.basename(wr.wait()) == "step_000004.bin"
