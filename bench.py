@@ -29,6 +29,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 UPDATE_BYTES_PER_PARAM = 28
 STEP_BYTES_PER_PARAM = 32
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_update_vec_andrea120m_pmc.md")
+CONFIG_WORKLOADS = ("flat262k", "andrea12m", "andrea120m_stress", "flat2e9")
 PROFILE_EVERY = 10
 KERNEL_SRC = os.path.join(ROOT, "resumable_checkpoint_state_amd", "csrc", "rcs.hip")
 
@@ -55,12 +56,16 @@ def kernel_source_hash(text: bytes | None = None) -> str:
     return hashlib.sha256(code).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per update launch from the committed rocprofv3 counter summary,
+def pmc_summary_for(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"adamw_update_vec_{workload}_pmc.md")
+
+
+def measured_traffic(path: str = PMC_SUMMARY):
+    """HBM bytes per update launch from a committed rocprofv3 counter summary,
     or None when there is none or the kernel source changed since."""
-    if not os.path.exists(PMC_SUMMARY):
+    if not os.path.exists(path):
         return None
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         text = f.read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
@@ -151,10 +156,42 @@ def async_pack_overlap(rcs, step, stream, w, m, v, buf, n, k=60):
             "snapshot_ms": snap_ms, "snapshot_GBps_24B_per_param": 24 * n / snap_ms / 1e6}
 
 
+def writer_cadence(rcs, step, stream, w, m, v, n, every=10, submits=4):
+    """The library's asynchronous writer at a cadence far shorter than one
+    disk write: `every` update steps between submits. Each submit's host
+    blocking time: it waits only while the host image it reuses (two
+    submits back) is still being written, so the first two return at once."""
+    import shutil
+    import tempfile
+
+    import torch
+
+    d = tempfile.mkdtemp(prefix="rcs_writer_", dir=os.environ.get("TMPDIR", "/tmp"))
+    try:
+        wr = rcs.CkptWriter(d, n, keep=2)
+        blocks = []
+        for k in range(submits):
+            for _ in range(every):
+                step()
+            t0 = time.perf_counter()
+            wr.submit(k + 1, w, m, v, stream=stream)
+            blocks.append((time.perf_counter() - t0) * 1e3)
+        t0 = time.perf_counter()
+        wr.wait()
+        drain = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        wr.close()
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    return {"writer_cadence_steps": every, "writer_submit_block_ms": blocks,
+            "writer_drain_ms": drain}
+
+
 def sharded_rate(rcs, w, m, v, world=8):
-    """Save and load of a sharded checkpoint (world simulated ranks): per-rank
-    pack, atomic shard writes with fsync, sha256, manifest; load verifies all
-    hashes before unpacking."""
+    """Save and load of a sharded checkpoint (world simulated ranks) through
+    one ShardedCheckpointer: per-rank pack into its staging buffer, atomic
+    shard writes with fsync, sha256, the manifest as the commit; load verifies
+    every shard, then reads each again and unpacks it."""
     import shutil
     import tempfile
 
@@ -162,16 +199,20 @@ def sharded_rate(rcs, w, m, v, world=8):
 
     d = tempfile.mkdtemp(prefix="rcs_shards_", dir=os.environ.get("TMPDIR", "/tmp"))
     try:
+        ck = sharded.ShardedCheckpointer(d, w.numel(), world)  # staging made here, once
         t0 = time.perf_counter()
-        sharded.save_sharded(d, 1, w, m, v, world)
+        ck.save(1, w, m, v)
         t_save = time.perf_counter() - t0
         t0 = time.perf_counter()
-        sharded.load_sharded(d, world, w, m, v)
+        ck.save(2, w, m, v)  # replaces the first: commit, then the old shards go
+        t_save2 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        ck.load(w, m, v)
         t_load = time.perf_counter() - t0
     finally:
         shutil.rmtree(d, ignore_errors=True)
     return {"sharded_world": world, "sharded_save_ms": t_save * 1e3,
-            "sharded_load_ms": t_load * 1e3}
+            "sharded_second_save_ms": t_save2 * 1e3, "sharded_load_ms": t_load * 1e3}
 
 
 def file_write_rate(rcs, buf):
@@ -261,6 +302,159 @@ def torch_reference(torch, wl, w, grads, steps: int) -> dict:
             "streaming_GBps": streaming}
 
 
+def measure_steps(torch, rcs, step, stream, steps: int) -> dict:
+    """Times `steps` calls of step() on `stream` three ways: the timed region
+    (events around all of them; on one step in PROFILE_EVERY the library has
+    the kernel dispatches stamp HIP events, giving the norm and update kernel
+    times), the same without per-kernel events, and with an event between
+    consecutive steps (median and p90 per step)."""
+    rcs.profile_enable(True, max(steps, 1), PROFILE_EVERY)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    norm_ms, upd_ms, rec = rcs.profile_read()
+    rcs.profile_enable(False)
+    ms_step = ev0.elapsed_time(ev1) / steps
+
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_noev = ev0.elapsed_time(ev1) / steps
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for k in range(steps):
+        step()
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps))
+    return {"ms_step": ms_step, "ms_step_noev": ms_step_noev, "wall_s": wall,
+            "median_us": per_step[len(per_step) // 2],
+            "p90_us": per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)],
+            "norm_us": norm_ms / rec * 1e3, "update_us": upd_ms / rec * 1e3, "recorded": rec}
+
+
+def update_kernel_name(n: int) -> str:
+    # the arrays here are 16-byte aligned; up to 8,388,608 elements the library's
+    # update kernel also does the final norm reduction (two launches per step)
+    return "adamw_update_vec_fold" if 4 <= n <= 8_388_608 else "adamw_update_vec"
+
+
+def config_leg(torch, rcs, workloads, name: str, steps: int, warmup: int,
+               cpu_seconds: float | None) -> dict:
+    """One more workload timed like the headline one (its own buffers, four
+    gradient buffers in rotation, resident before timing), with its update
+    kernel's roofline, then, unless cpu_seconds is None, the oracle on a
+    bounded sample of it."""
+    wl = workloads.WORKLOADS[name]
+    n = wl.n
+    dev = torch.device("cuda:0")
+    _log(f"[bench] config {name} n={n:,}")
+    w = workloads.init_params(wl, device=dev)
+    m, v = workloads.zeros_like_state(n, device=dev)
+    grads = [workloads.grads(wl, t, device=dev) for t in range(1, 5)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t = 0
+
+    def step():
+        nonlocal t
+        t += 1
+        rcs.adamw_clip_step(w, grads[(t - 1) % 4], m, v, t, wl.lr, wl.wd, wl.clip, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    meas = measure_steps(torch, rcs, step, stream, steps)
+    achieved = UPDATE_BYTES_PER_PARAM * n / (meas["update_us"] / 1e6) / 1e9
+    out = {"workload": name, "n_params": n, "steps": steps, "ms_per_step": meas["ms_step"],
+           "params_per_s": n / (meas["ms_step"] / 1e3),
+           "model_GBps": STEP_BYTES_PER_PARAM * n / (meas["ms_step"] / 1e3) / 1e9,
+           "step_us_median": meas["median_us"], "step_us_p90": meas["p90_us"],
+           "kernels_us": {"norm": meas["norm_us"], "adamw_update": meas["update_us"]},
+           "roofline": {"bound": "hbm", "kernel": update_kernel_name(n), "achieved": achieved,
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                        "traffic": measured_traffic(pmc_summary_for(name)),
+                        "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
+           "description": wl.description}
+    if name == "flat2e9":
+        out["ceilings"] = ceilings(torch, n, (w, grads[0], m, v))
+    del w, m, v, grads
+    torch.cuda.empty_cache()
+    if cpu_seconds is None:
+        out["cpu_baseline"] = None
+        out["cpu_baseline_skipped"] = ("the oracle's state for 2e9 parameters (24 GB) plus its "
+                                       "gradient does not fit a bounded host sample; its "
+                                       "per-element rate is the ANDREA-120M figure")
+    else:
+        out["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
+    return out
+
+
+def _ceiling_lib():
+    import ctypes
+
+    path = os.path.join(ROOT, "resumable_checkpoint_state_amd", "libceilings.so")
+    L = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.rcs_ceiling_blocks.argtypes = [i64]
+    L.rcs_ceiling_blocks.restype = i64
+    L.rcs_ceiling_read.argtypes = [vp, i64, vp, vp]
+    L.rcs_ceiling_read.restype = ctypes.c_int
+    L.rcs_ceiling_copy.argtypes = [vp, vp, i64, vp]
+    L.rcs_ceiling_copy.restype = ctypes.c_int
+    L.rcs_ceiling_4r3w.argtypes = [vp, vp, vp, vp, i64, vp]
+    L.rcs_ceiling_4r3w.restype = ctypes.c_int
+    return L
+
+
+def ceilings(torch, n: int, arrays=None, reps: int = 10) -> dict:
+    """What the chip's HBM gives three streaming patterns over float32[n]:
+    a read (the norm pass's shape), a copy and the update's 4-read/3-write
+    pattern with one add per element (both in the update's shape), each the
+    average of `reps` launches timed with events on the current stream.
+    `arrays` (w, g, m, v) are reused (and overwritten) when given."""
+    L = _ceiling_lib()
+    n4 = n // 4
+    made = arrays is None
+    if made:
+        arrays = [torch.ones(4 * n4, device="cuda") for _ in range(4)]
+    p = [a.data_ptr() for a in arrays]
+    out_buf = torch.empty(max(1, L.rcs_ceiling_blocks(n4)), device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    r = timed(lambda: L.rcs_ceiling_read(p[0], n4, out_buf.data_ptr(), st))
+    c = timed(lambda: L.rcs_ceiling_copy(p[0], p[1], n4, st))
+    k = timed(lambda: L.rcs_ceiling_4r3w(p[0], p[1], p[2], p[3], n4, st))
+    if made:
+        del arrays
+        torch.cuda.empty_cache()
+    return {"n": 4 * n4, "read_GBps": 16 * n4 / r / 1e9, "copy_GBps": 32 * n4 / c / 1e9,
+            "pattern_4r3w_GBps": 112 * n4 / k / 1e9, "read_us": r * 1e6, "copy_us": c * 1e6,
+            "pattern_4r3w_us": k * 1e6}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +464,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-ckpt", action="store_true", help="skip the pack/unpack leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads (small, ANDREA-12M, stress, 2e9)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
+                    help="oracle time budget per other workload")
     ap.add_argument("--no-torch-ref", action="store_true",
                     help="skip timing PyTorch's fused AdamW + clip on the same inputs")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GiB",
@@ -326,49 +524,14 @@ def main() -> int:
     # timed region: K steps; on one step in PROFILE_EVERY the library has the
     # kernel dispatches themselves stamp HIP events (start/end of the norm
     # kernels and of the update kernel) on the stream they run on
-    rcs.profile_enable(True, max(args.steps, 1), PROFILE_EVERY)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    norm_ms, upd_ms, rec = rcs.profile_read()
-    rcs.profile_enable(False)
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    meas = measure_steps(torch, rcs, step, stream, args.steps)
+    ms_step = meas["ms_step"]
     _log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step "
-         f"(wall {wall / args.steps * 1e6:.1f} us/step); per-kernel events on {rec} of them")
+         f"(wall {meas['wall_s'] / args.steps * 1e6:.1f} us/step); per-kernel events on "
+         f"{meas['recorded']} of them")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # a second pass without per-kernel events, to show their overhead
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_noev = ev0.elapsed_time(ev1) / args.steps
-
-    # a third pass with an event between consecutive steps: per-step spread
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for k in range(args.steps):
-        step()
-        evs[k + 1].record(stream)
-    torch.cuda.synchronize()
-    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(args.steps))
-    step_median_us = per_step[len(per_step) // 2]
-    step_p90_us = per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)]
-
-    # the arrays here are 16-byte aligned; up to 8,388,608 elements the library's
-    # update kernel also does the final norm reduction (two launches per step)
-    update_kernel = "adamw_update_vec_fold" if 4 <= n <= 8_388_608 else "adamw_update_vec"
-    upd_s = upd_ms / rec / 1e3
-    norm_s = norm_ms / rec / 1e3
+    upd_s = meas["update_us"] / 1e6
     achieved = UPDATE_BYTES_PER_PARAM * n / upd_s / 1e9
     params_per_s = n / (ms_step / 1e3)
     model_gbps = STEP_BYTES_PER_PARAM * n / (ms_step / 1e3) / 1e9
@@ -393,14 +556,13 @@ def main() -> int:
         "model_frac_of_hbm_peak": model_gbps / HBM_PEAK_GBPS,
         # norm: grad_norm_partial's start to the end of the last norm kernel
         # (grad_norm_final, or grad_norm_partial when the update folds it in)
-        "kernels_us": {"norm": norm_s * 1e6, "adamw_update": upd_s * 1e6},
-        "ms_per_step_without_kernel_events": ms_step_noev,
-        "step_us_median": step_median_us,
-        "step_us_p90": step_p90_us,
-        "roofline": {"bound": "hbm", "kernel": update_kernel, "achieved": achieved,
+        "kernels_us": {"norm": meas["norm_us"], "adamw_update": meas["update_us"]},
+        "ms_per_step_without_kernel_events": meas["ms_step_noev"],
+        "step_us_median": meas["median_us"],
+        "step_us_p90": meas["p90_us"],
+        "roofline": {"bound": "hbm", "kernel": update_kernel_name(n), "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     # the committed counters were taken at the ANDREA-120M size
-                     "traffic": measured_traffic() if n == workloads.ANDREA120M_N else None,
+                     "traffic": measured_traffic(pmc_summary_for(wl.name)),
                      "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
     }
 
@@ -426,6 +588,9 @@ def main() -> int:
     zero_s = ev0.elapsed_time(ev1) / reps / 1e3
     result["grad_zero"] = {"us": zero_s * 1e6, "GBps_4B_per_param": 4 * n / zero_s / 1e9}
     del scratch
+
+    # what the HBM gives the same streaming patterns at this size (fresh buffers)
+    result["ceilings"] = ceilings(torch, n)
 
     if not args.no_torch_ref:
         ref = torch_reference(torch, wl, w, grads, min(args.steps, 50))
@@ -454,7 +619,8 @@ def main() -> int:
                           "unpack_GBps_host_link": nb / unpack_s / 1e9,
                           "pack_ms": pack_s * 1e3, "unpack_ms": unpack_s * 1e3}
         result["ckpt"].update(async_pack_overlap(rcs, step, stream, w, m, v, buf, n))
-        for leg in (lambda: file_write_rate(rcs, buf), lambda: sharded_rate(rcs, w, m, v)):
+        for leg in (lambda: file_write_rate(rcs, buf), lambda: sharded_rate(rcs, w, m, v),
+                    lambda: writer_cadence(rcs, step, stream, w, m, v, n)):
             try:  # a full or read-only TMPDIR must not cost the step measurement
                 result["ckpt"].update(leg())
             except (OSError, RuntimeError) as e:
@@ -463,8 +629,18 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         _log(f"[bench] CPU baseline: the oracle for about {args.cpu_seconds:.0f} s")
-        del grads
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+
+    if not args.no_configs:
+        # the other workloads, timed the same way after the headline one; the
+        # headline's buffers are released first
+        del w, m, v, grads
+        torch.cuda.empty_cache()
+        cpu_s = None if args.no_cpu_baseline else args.config_cpu_seconds
+        result["configs"] = {
+            name: config_leg(torch, rcs, workloads, name, args.steps, args.warmup,
+                             None if name == "flat2e9" else cpu_s)
+            for name in CONFIG_WORKLOADS if name != wl.name}
 
     print(json.dumps(result), flush=True)
     return 0

@@ -22,6 +22,17 @@
  * Every call validates its arguments on the host before enqueuing anything and
  * returns one of the status codes below; a negative return means nothing was
  * enqueued (except RCS_EHIP, which reports a failed launch or copy).
+ *
+ * What the device-array checks can see: each array must be device (or
+ * managed) memory of the current device, and [p, p + 4 n) must lie inside the
+ * allocation the runtime reports for p (RCS_ESIZE otherwise). That is the
+ * allocation as the HIP runtime made it: a caller's sub-allocator (PyTorch's
+ * caching allocator, an arena) carves many arrays out of one allocation, and an
+ * array too short for n that still ends inside that allocation cannot be told
+ * from a long enough one, so the call would read and write past it. Memory for
+ * which the runtime reports no range (e.g. some virtual-memory mappings) is
+ * accepted without the length check. Callers that carve arrays out of larger
+ * blocks must pass the true n.
  */
 #ifndef RCS_H
 #define RCS_H
@@ -146,8 +157,11 @@ int adamw_clip_step_noalloc(float *w, const float *g, float *m, float *v, int64_
 
 /*
  * The pre-clip global norm alone: sqrt(sum_i (double)g[i]^2), same kernels and
- * order as adamw_clip_step. norm_out is device memory or pinned host memory
- * and receives one float64 once the stream reaches this call.
+ * order as adamw_clip_step (the per-block partial sums and the final reduction
+ * of the backprop lesson's pairing-rule table, without the scale). The resume
+ * page ("Task and Prerequisites") records this norm before clipping, to spot
+ * numerical faults. norm_out is device memory or pinned host memory and
+ * receives one float64 once the stream reaches this call.
  */
 int grad_global_norm(const float *g, int64_t n, double *norm_out, hipStream_t stream);
 

@@ -3,20 +3,23 @@
 // chip's HBM gives that pattern. Not part of the library's C ABI and not on
 // the training path: they compute nothing of the method.
 //
-// All three use the update's launch shape (one wave per block, one 16-byte
-// vector of each array per lane, streaming loads and stores, block b working
-// in contiguous region b % 8 of the vectors), over float32 arrays of n4 16-byte
-// vectors:
-//   rcs_ceiling_read:  reads a; each block writes one float (sum of its lanes'
-//                      x components, so the loads are not dropped): 16 B/vector.
+// Over float32 arrays of n4 16-byte vectors:
+//   rcs_ceiling_read:  reads a in the norm pass's shape (at most 256 blocks of
+//                      512 lanes, 4 streaming 16-byte loads in flight per
+//                      lane, grid-stride); each block writes one float (the
+//                      sum of everything it read, so no load is dropped or
+//                      narrowed): 16 B/vector.
+// and in the update's launch shape (one wave per block, one 16-byte vector of
+// each array per lane, streaming loads and stores, block b working in
+// contiguous region b % 8 of the vectors):
 //   rcs_ceiling_copy:  b = a: 32 B/vector.
 //   rcs_ceiling_4r3w:  reads w, g, m, v and writes w, m, v with one add per
 //                      element (w += g, m += g, v += g): the update's 28 B per
 //                      4 elements with trivial arithmetic.
 // Each returns 0 after a successful launch, -1 for bad arguments, -4 if the
 // launch failed. Pointers must be 16-byte aligned device memory holding n4
-// vectors (rcs_ceiling_read's `out`: one float per block, see
-// rcs_ceiling_blocks).
+// vectors (rcs_ceiling_read's `out`: one float per block, rcs_ceiling_blocks
+// of them).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -34,13 +37,38 @@ __device__ __forceinline__ int64_t chunk_of_block() {
     return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
-__global__ __launch_bounds__(kLanes) void ceiling_read(const f32x4 *__restrict__ a, int64_t n4,
-                                                       float *__restrict__ out) {
-    const int64_t i = chunk_of_block() * kLanes + threadIdx.x;
+constexpr int kReadLanes = 512;
+constexpr int kReadUnroll = 4;
+constexpr int kReadMaxBlocks = 256;
+
+__global__ __launch_bounds__(kReadLanes) void ceiling_read(const f32x4 *__restrict__ a, int64_t n4,
+                                                           float *__restrict__ out) {
+    __shared__ float lds[kReadLanes / 64];
     float x = 0.0f;
-    if (i < n4) x = __builtin_nontemporal_load(a + i).x;
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kLanes);
-    if (threadIdx.x == 0) out[blockIdx.x] = x;
+    const int64_t chunk = (int64_t)kReadLanes * kReadUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * chunk; base < n4; base += (int64_t)gridDim.x * chunk) {
+        f32x4 v[kReadUnroll];
+#pragma unroll
+        for (int j = 0; j < kReadUnroll; ++j) {
+            const int64_t i = base + (int64_t)j * kReadLanes + threadIdx.x;
+            v[j] = (i < n4) ? __builtin_nontemporal_load(a + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < kReadUnroll; ++j) x += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    }
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x / 64] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int k = 0; k < kReadLanes / 64; ++k) t += lds[k];
+        out[blockIdx.x] = t;
+    }
+}
+
+int64_t read_blocks(int64_t n4) {
+    const int64_t b = (n4 + (int64_t)kReadLanes * kReadUnroll - 1) / ((int64_t)kReadLanes * kReadUnroll);
+    return b < kReadMaxBlocks ? b : kReadMaxBlocks;
 }
 
 __global__ __launch_bounds__(kLanes) void ceiling_copy(const f32x4 *__restrict__ a,
@@ -75,12 +103,12 @@ int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 extern "C" {
 
-// Blocks (and so floats of rcs_ceiling_read's output) for n4 vectors.
-int64_t rcs_ceiling_blocks(int64_t n4) { return (n4 + kLanes - 1) / kLanes; }
+// Blocks of rcs_ceiling_read (and so floats of its output) for n4 vectors.
+int64_t rcs_ceiling_blocks(int64_t n4) { return n4 < 1 ? 0 : read_blocks(n4); }
 
 int rcs_ceiling_read(const float *a, int64_t n4, float *out, hipStream_t stream) {
     if (!ok16(a) || out == nullptr || n4 < 1 || n4 > ((int64_t)1 << 36)) return -1;
-    hipLaunchKernelGGL(ceiling_read, grid_of(n4), dim3(kLanes), 0, stream,
+    hipLaunchKernelGGL(ceiling_read, dim3((unsigned)read_blocks(n4)), dim3(kReadLanes), 0, stream,
                        reinterpret_cast<const f32x4 *>(a), n4, out);
     return launched();
 }

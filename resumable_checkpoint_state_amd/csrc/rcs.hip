@@ -840,9 +840,11 @@ int get_workspace(hipStream_t stream, Workspace **out) {
 }
 
 // p must be device (or managed) memory of the current device and the range
-// [p, p + bytes) must lie inside one allocation. Memory the runtime cannot
-// report a range for (e.g. virtual-memory mappings) is accepted without the
-// length check.
+// [p, p + bytes) must lie inside the allocation the runtime reports for p.
+// That allocation is the runtime's own: an array carved by a sub-allocator out
+// of a larger block passes as long as it ends inside that block, whatever its
+// true length. Memory the runtime cannot report a range for (e.g. virtual-
+// memory mappings) is accepted without the length check.
 int check_device_range(const void *p, int64_t bytes) {
     if (p == nullptr) return RCS_EINVAL;
     int dev = -1;

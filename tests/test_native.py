@@ -137,3 +137,18 @@ def test_c_program_trains_and_saves_on_the_gpu(tmp_path, n):
         assert max_ulp(arr, ref) <= 2, j
     assert os.path.basename(paths["writer"]) == "step_000003.bin"
     assert open(paths["writer"], "rb").read() == raw
+
+
+@pytest.mark.gpu
+def test_c_abi_refuses_exact_size_short_buffers(tmp_path):
+    """hipMalloc'd arrays of exactly their own size, one of them shorter than
+    n: every call that takes device arrays returns RCS_ESIZE and nothing is
+    launched (the arrays keep a byte pattern any kernel or copy would
+    overwrite)."""
+    exe = tmp_path / "abi_short_buffers"
+    libdir = os.path.dirname(rcs.LIB_PATH)
+    _run(["gcc", "-std=c11", "-Wall", "-Werror", *HIP_DEFS,
+          os.path.join(NATIVE, "abi_short_buffers.c"), f"-L{libdir}", "-l:librcs.so",
+          f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{libdir}", f"-Wl,-rpath,{ROCM}/lib",
+          "-o", str(exe)])
+    assert "abi short buffers ok" in _run([str(exe)], timeout=120)
