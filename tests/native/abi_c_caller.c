@@ -24,6 +24,11 @@ int main(void) {
     EXPECT(adamw_clip_step(NULL, NULL, NULL, NULL, 16, 1, 1e-3f, 0.0f, 1.0f, 0) == RCS_EINVAL);
     EXPECT(adamw_clip_step_accum(NULL, NULL, NULL, NULL, 16, 1, 1e-3f, 0.0f, 1.0f, 0.5f, 0) ==
            RCS_EINVAL);
+    EXPECT(adamw_clip_step_noalloc(NULL, NULL, NULL, NULL, 16, 1, 1e-3f, 0.0f, 1.0f, NULL, 0) ==
+           RCS_EINVAL);
+    EXPECT(adamw_clip_step_noalloc((float *)0x1000, (float *)0x1000, (float *)0x1000,
+                                   (float *)0x1000, RCS_MAX_N + 1, 1, 1e-3f, 0.0f, 1.0f, NULL,
+                                   0) == RCS_EINVAL);
     EXPECT(grad_zero(NULL, 16, 0) == RCS_EINVAL);
     EXPECT(grad_zero((float *)0x1000, 0, 0) == RCS_EINVAL);
     memset(buf, 0, sizeof buf);

@@ -71,6 +71,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: rejected before any device
 def test_adamw_clip_step_rejects_bad_scalars(L, n, t, lr, wd, clip):
     rc = L.adamw_clip_step(FAKE, FAKE, FAKE, FAKE, n, t, lr, wd, clip, None)
     assert rc == rcs.EINVAL
+    rc = L.adamw_clip_step_noalloc(FAKE, FAKE, FAKE, FAKE, n, t, lr, wd, clip, None, None)
+    assert rc == rcs.EINVAL
 
 
 def test_null_pointers_rejected(L):
