@@ -344,6 +344,29 @@ def measure_steps(torch, rcs, step, stream, steps: int) -> dict:
             "norm_us": norm_ms / rec * 1e3, "update_us": upd_ms / rec * 1e3, "recorded": rec}
 
 
+def host_cost(torch, rcs, step, stream, w, g, m, v, wl, calls: int = 200) -> dict:
+    """Host time per enqueued update where the step is launch-bound: through
+    the Python binding (argument checks on the tensors, then the C call) and
+    through the C ABI with the pointers already extracted (ctypes only); the
+    library's own host work (validation, workspace lookup, two launches) is in
+    both. Wall time of `calls` back-to-back calls after a synchronize."""
+    L = rcs.lib()
+    ptrs = (w.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr())
+    n, raw = w.numel(), stream.cuda_stream
+    out = {}
+    for label, fn in (("binding", lambda t: rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd,
+                                                                 wl.clip, stream=stream)),
+                      ("c_abi", lambda t: L.adamw_clip_step(*ptrs, n, t, wl.lr, wl.wd, wl.clip,
+                                                            raw))):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(calls):
+            fn(k + 1)
+        out[label] = (time.perf_counter() - t0) / calls * 1e6
+        torch.cuda.synchronize()
+    return out
+
+
 def update_kernel_name(n: int) -> str:
     # the arrays here are 16-byte aligned; up to 8,388,608 elements the library's
     # update kernel also does the final norm reduction (two launches per step)
@@ -375,6 +398,7 @@ def config_leg(torch, rcs, workloads, name: str, steps: int, warmup: int,
     for _ in range(warmup):
         step()
     meas = measure_steps(torch, rcs, step, stream, steps)
+    host = host_cost(torch, rcs, step, stream, w, grads[0], m, v, wl) if n <= 1_000_000 else None
     achieved = UPDATE_BYTES_PER_PARAM * n / (meas["update_us"] / 1e6) / 1e9
     out = {"workload": name, "n_params": n, "steps": steps, "ms_per_step": meas["ms_step"],
            "params_per_s": n / (meas["ms_step"] / 1e3),
@@ -386,6 +410,8 @@ def config_leg(torch, rcs, workloads, name: str, steps: int, warmup: int,
                         "traffic": measured_traffic(pmc_summary_for(name)),
                         "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
            "description": wl.description}
+    if host is not None:
+        out["host_us_per_call"] = host
     if name == "flat2e9":
         out["ceilings"] = ceilings(torch, n, (w, grads[0], m, v))
     del w, m, v, grads

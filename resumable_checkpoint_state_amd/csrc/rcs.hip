@@ -313,9 +313,10 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
     __builtin_nontemporal_store(x, p);
 }
 
-// An array among g, m, v at another 16-byte phase than w: its body xb (the
-// element matching w's first body element) lies q = 1-3 floats past a 16-byte
-// boundary, so lane i's four elements xb[4i .. 4i+3] straddle two aligned
+// An array at another 16-byte phase than the anchor (the array whose body
+// starts on the 256-byte boundary): its body xb (the element matching the
+// anchor's first body element) lies q = 1-3 floats past a 16-byte boundary,
+// so lane i's four elements xb[4i .. 4i+3] straddle two aligned
 // vectors of the array. Every access stays a 16-byte aligned one: each lane
 // loads the aligned vector holding its first element (its positions q..3 are
 // the lane's first 4 - q elements) and takes the rest (positions 0..q-1 of the
@@ -330,9 +331,10 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
 
 // xb[4i .. 4i+3] for vector ic (i clamped to the body). first: ic is vector 0
 // and the aligned vector holding xb[0] starts before the array (head < q):
-// the lane's elements of it are read one by one. own: the next lane does not hold the next aligned vector (this is
-// the wave's last lane or the body's last vector): read positions 0..q-1 of it
-// one by one. Every lane of the wave must call this (cross-lane shifts).
+// the lane's elements of it are read one by one. own: the next lane does not
+// hold the next aligned vector (this is the wave's last lane or the body's
+// last vector): positions 0..q-1 of it are read one by one. Every lane of the
+// wave must call this (cross-lane shifts).
 __device__ __forceinline__ f32x4 ld_shifted(const float *__restrict__ xb, int q, int64_t ic,
                                             bool first, bool own) {
     f32x4 a;
@@ -560,9 +562,10 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_scalar(
 // The pages' third clip kernel on its own, for callers that need the clipped
 // gradient itself: g *= s in place (skipped when the norm is not finite). Same
 // float32 product as the update's g * s. g points `head` (0-63) elements past
-// the array's start, at a 16-byte boundary, and n counts from there. Lanes past the end re-read the last vector and discard it (the host
-// guarantees n >= 4); block 0 also scales the head elements and the last
-// block the n % 4 trailing ones. FOLD as in update_body: the record from
+// the array's start, at a 16-byte boundary, and n counts from there. Lanes
+// past the end re-read the last vector and discard it (the host guarantees
+// n >= 4); block 0 also scales the head elements and the last block the n % 4
+// trailing ones. FOLD as in update_body: the record from
 // grad_norm_final, or the final reduction at the head of every block.
 template <bool FOLD>
 __device__ __forceinline__ void scale_body(f32x4 *__restrict__ g, int64_t n, int head,
@@ -684,7 +687,9 @@ __global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *_
         const float *sb = src + head;
         f32x4 x;
         if (q == 0) x = ld_stream(reinterpret_cast<const f32x4 *>(sb) + ic);
-        else x = ld_shifted(sb, q, ic, ic == 0 && head < q, threadIdx.x == kWave - 1 || ic == nb4 - 1);
+        else
+            x = ld_shifted(sb, q, ic, ic == 0 && head < q,
+                           threadIdx.x == kWave - 1 || ic == nb4 - 1);
         if (i < nb4) st_stream(reinterpret_cast<f32x4 *>(dst + head) + i, x);
     }
     if (blockIdx.x == 0) {
@@ -908,8 +913,8 @@ int head_of(const void *p, int64_t n) {
 }
 
 // a1 alone. ev0 / ev1 (optional, profiling) take the kernel's start / end.
-void launch_partial(const float *g, int64_t n, float gscale, const NormBuffers *ws, hipStream_t stream,
-                    hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+void launch_partial(const float *g, int64_t n, float gscale, const NormBuffers *ws,
+                    hipStream_t stream, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     const int head = head_of(g, n);
     hipExtLaunchKernelGGL(grad_norm_partial, dim3(norm_blocks(n)), dim3(kNormThreads), 0, stream,
                           ev0, ev1, 0, g, n, head, norm_nt_limit4(head >= 0 ? n - head : n),
