@@ -243,7 +243,10 @@ int ckpt_unpack(const void *host_buf, int64_t buf_bytes, int64_t n_expected, int
  * earlier copy out of it has finished. host_buf must not be read or reused
  * until ckpt_pack_wait(snapshot) returns (or copy_stream is synchronized).
  * Sizes: snapshot_bytes == ckpt_snapshot_bytes(n) == 12 n, buf_bytes ==
- * ckpt_bytes(n). The snapshot must not overlap w, m or v.
+ * ckpt_bytes(n). The snapshot must not overlap w, m or v (they may sit next
+ * to it in one allocation). The snapshot kernel writes each part in aligned
+ * 16-byte vectors and reads its source in aligned 16-byte vectors at any
+ * 4-byte phase (n >= 4, 4-byte aligned pointers; otherwise a 4-byte copy).
  */
 int64_t ckpt_snapshot_bytes(int64_t n);
 int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, const float *v,
@@ -304,25 +307,30 @@ int rcs_signals_poll(void);
  * Asynchronous step-file writer (the sharded-resume lesson's production
  * patterns: asynchronous, atomic, keep the newest K; the checkpoints page's
  * SIGTERM save, after which the caller waits and exits). The writer owns a
- * device snapshot (12 n bytes), a pinned host buffer (8 + 12 n bytes), a copy
- * stream and one worker thread, all made by rcs_ckpt_writer_create on the
+ * device snapshot (12 n bytes), two pinned host images (8 + 12 n bytes
+ * each), a copy stream and one worker thread, all made by rcs_ckpt_writer_create on the
  * current device and freed by rcs_ckpt_writer_destroy. dir must exist (as
  * for ckpt_file_write); a missing or unwritable one makes each write fail
  * with RCS_EIO.
  *
- * rcs_ckpt_writer_submit: waits until the previous write has finished (if
- * that write failed, returns its status and submits nothing), then enqueues
- * ckpt_pack_async of (step, w, m, v) -- a snapshot kernel on compute_stream,
- * the device-to-host copy on the writer's copy stream -- and returns; the
- * worker waits for the copy, writes <dir>/step_%06d.bin atomically
- * (ckpt_file_write) and keeps the `keep` newest files (ckpt_file_rotate).
- * w, m, v may be updated by later work on compute_stream right away. Must be
- * called with the writer's device current; submits are serialized.
+ * The writer has two pinned host images of 8 + 12 n bytes each, so that one
+ * can receive a copy while the other is being written to disk.
+ * rcs_ckpt_writer_submit: waits while the host image it will use is still
+ * being written (the save two submits back); if an earlier write failed,
+ * returns that status and submits nothing; then enqueues ckpt_pack_async of
+ * (step, w, m, v) -- a snapshot kernel on compute_stream, the device-to-host
+ * copy into the image on the writer's copy stream -- and returns; the worker
+ * waits for the copy, writes <dir>/step_%06d.bin atomically (ckpt_file_write)
+ * and keeps the `keep` newest files (ckpt_file_rotate), one job at a time in
+ * submit order. w, m, v may be updated by later work on compute_stream right
+ * away. Must be called with the writer's device current; submits are
+ * serialized.
  * rcs_ckpt_writer_wait: blocks until no write is in flight and returns the
- * status of the last finished one; path_out (optional, path_cap bytes)
- * receives the path it wrote. Both are reported once: a second wait returns
- * RCS_OK and "". A path_cap too small for the path returns RCS_EINVAL and
- * leaves the status and path to the next wait.
+ * first failure not yet reported (else RCS_OK); path_out (optional, path_cap
+ * bytes) receives the newest path written since the last wait. Both are
+ * reported once: a second wait returns RCS_OK and "". A path_cap too small
+ * for the path returns RCS_EINVAL and leaves the status and path to the next
+ * wait.
  * rcs_ckpt_writer_destroy: waits, stops the worker, frees everything; returns
  * the status of the last write not yet reported. NULL is a no-op.
  */
