@@ -30,7 +30,6 @@ UPDATE_BYTES_PER_PARAM = 28
 STEP_BYTES_PER_PARAM = 32
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_update_vec_andrea120m_pmc.md")
 CONFIG_WORKLOADS = ("flat262k", "andrea12m", "andrea120m_stress", "flat2e9")
-PROFILE_EVERY = 10
 KERNEL_SRC = os.path.join(ROOT, "resumable_checkpoint_state_amd", "csrc", "rcs.hip")
 
 
@@ -304,11 +303,11 @@ def torch_reference(torch, wl, w, grads, steps: int) -> dict:
 
 def measure_steps(torch, rcs, step, stream, steps: int) -> dict:
     """Times `steps` calls of step() on `stream` three ways: the timed region
-    (events around all of them; on one step in PROFILE_EVERY the library has
-    the kernel dispatches stamp HIP events, giving the norm and update kernel
-    times), the same without per-kernel events, and with an event between
-    consecutive steps (median and p90 per step)."""
-    rcs.profile_enable(True, max(steps, 1), PROFILE_EVERY)
+    itself (events around all of them, nothing else instrumented), the same
+    again with every step's kernel dispatches stamping HIP events (the norm
+    kernels' and the update kernel's start and end, on the stream they run
+    on: the per-kernel averages over all `steps` launches), and with an event
+    between consecutive steps (median and p90 per step)."""
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -318,17 +317,18 @@ def measure_steps(torch, rcs, step, stream, steps: int) -> dict:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    norm_ms, upd_ms, rec = rcs.profile_read()
-    rcs.profile_enable(False)
     ms_step = ev0.elapsed_time(ev1) / steps
 
+    rcs.profile_enable(True, max(steps, 1), 1)
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms_step_noev = ev0.elapsed_time(ev1) / steps
+    ms_step_ev = ev0.elapsed_time(ev1) / steps
+    norm_ms, upd_ms, rec = rcs.profile_read()
+    rcs.profile_enable(False)
 
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
@@ -338,7 +338,7 @@ def measure_steps(torch, rcs, step, stream, steps: int) -> dict:
         evs[k + 1].record(stream)
     torch.cuda.synchronize()
     per_step = sorted(evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps))
-    return {"ms_step": ms_step, "ms_step_noev": ms_step_noev, "wall_s": wall,
+    return {"ms_step": ms_step, "ms_step_kernel_events": ms_step_ev, "wall_s": wall,
             "median_us": per_step[len(per_step) // 2],
             "p90_us": per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)],
             "norm_us": norm_ms / rec * 1e3, "update_us": upd_ms / rec * 1e3, "recorded": rec}
@@ -547,14 +547,13 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; on one step in PROFILE_EVERY the library has the
-    # kernel dispatches themselves stamp HIP events (start/end of the norm
-    # kernels and of the update kernel) on the stream they run on
+    # timed region: K uninstrumented steps; then K more whose kernel dispatches
+    # stamp HIP events (the kernel averages); then K with per-step events
     meas = measure_steps(torch, rcs, step, stream, args.steps)
     ms_step = meas["ms_step"]
     _log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step "
-         f"(wall {meas['wall_s'] / args.steps * 1e6:.1f} us/step); per-kernel events on "
-         f"{meas['recorded']} of them")
+         f"(wall {meas['wall_s'] / args.steps * 1e6:.1f} us/step); kernel averages over "
+         f"{meas['recorded']} instrumented steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     upd_s = meas["update_us"] / 1e6
@@ -583,7 +582,7 @@ def main() -> int:
         # norm: grad_norm_partial's start to the end of the last norm kernel
         # (grad_norm_final, or grad_norm_partial when the update folds it in)
         "kernels_us": {"norm": meas["norm_us"], "adamw_update": meas["update_us"]},
-        "ms_per_step_without_kernel_events": meas["ms_step_noev"],
+        "ms_per_step_with_kernel_events": meas["ms_step_kernel_events"],
         "step_us_median": meas["median_us"],
         "step_us_p90": meas["p90_us"],
         "roofline": {"bound": "hbm", "kernel": update_kernel_name(n), "achieved": achieved,
