@@ -176,11 +176,14 @@ class ShardedCheckpointer:
     """Sharded save and load of (w, m, v) over float32[n] for a fixed world
     size, through one pinned staging buffer made here and reused."""
 
-    def __init__(self, directory, n: int, world_size: int):
+    def __init__(self, directory, n: int, world_size: int, pin_memory: bool = True):
+        """pin_memory=False makes a pageable staging buffer (host-only use,
+        e.g. verifying files on a machine without a GPU)."""
         self.dir, self.n, self.world_size = str(directory), int(n), int(world_size)
         self.ranges = shard_ranges(self.n, self.world_size)
+        self.pin_memory = bool(pin_memory)
         largest = max(ckpt_bytes(k) for _, k in self.ranges)
-        self.staging = torch.empty(largest, dtype=torch.uint8, pin_memory=True)
+        self.staging = torch.empty(largest, dtype=torch.uint8, pin_memory=self.pin_memory)
         os.makedirs(self.dir, exist_ok=True)
 
     def save(self, step: int, w, m, v, wall_clock_seconds: float = 0.0,
@@ -224,7 +227,7 @@ class ShardedCheckpointer:
         man = _read_manifest(self.dir, self.world_size, self.n)
         need = max(ckpt_bytes(s.param_shard_numel) for s in man.shards)
         if need > self.staging.numel():  # a checkpoint split differently from this one
-            self.staging = torch.empty(need, dtype=torch.uint8, pin_memory=True)
+            self.staging = torch.empty(need, dtype=torch.uint8, pin_memory=self.pin_memory)
         host = self.staging.numpy()
         for s in man.shards:
             _read_shard(self.dir, man, s, host)

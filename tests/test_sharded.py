@@ -187,8 +187,6 @@ def _fake_ckpt(monkeypatch, fail_after_rank=None):
             return real(path, buf, nbytes)
 
     monkeypatch.setattr(sharded, "lib", lambda: Lib())
-    monkeypatch.setattr(sharded.torch, "empty",
-                        lambda k, dtype=None, pin_memory=False: torch.zeros(k, dtype=dtype))
 
 
 def test_crash_during_a_save_keeps_the_previous_checkpoint(tmp_path, monkeypatch):
@@ -198,12 +196,12 @@ def test_crash_during_a_save_keeps_the_previous_checkpoint(tmp_path, monkeypatch
     n, world = 4000, 4
     w, m, v = (torch.from_numpy(a) for a in _arrays(n, seed=5))
     _fake_ckpt(monkeypatch)
-    ck = sharded.ShardedCheckpointer(tmp_path, n, world)
+    ck = sharded.ShardedCheckpointer(tmp_path, n, world, pin_memory=False)
     man80 = ck.save(80, w, m, v)
     before = {f: open(tmp_path / f, "rb").read() for f in os.listdir(tmp_path)}
     for fail_after in (0, 2):
         _fake_ckpt(monkeypatch, fail_after_rank=fail_after)
-        ck = sharded.ShardedCheckpointer(tmp_path, n, world)
+        ck = sharded.ShardedCheckpointer(tmp_path, n, world, pin_memory=False)
         with pytest.raises(KeyboardInterrupt):
             ck.save(160, w * 2, m * 2, v * 2)
         man = sharded.verify_sharded(tmp_path, world, n)
@@ -212,7 +210,8 @@ def test_crash_during_a_save_keeps_the_previous_checkpoint(tmp_path, monkeypatch
             assert open(tmp_path / f, "rb").read() == data
     # a completed save then replaces it and removes the step-80 shards
     _fake_ckpt(monkeypatch)
-    man160 = sharded.ShardedCheckpointer(tmp_path, n, world).save(160, w * 2, m * 2, v * 2)
+    man160 = sharded.ShardedCheckpointer(tmp_path, n, world, pin_memory=False).save(
+        160, w * 2, m * 2, v * 2)
     assert sharded.verify_sharded(tmp_path, world, n).step == 160
     left = sorted(os.listdir(tmp_path))
     assert left == sorted(["manifest.json"] + [s.path for s in man160.shards])
@@ -224,7 +223,7 @@ def test_checkpointer_reuses_one_staging_buffer(tmp_path, monkeypatch):
     n, world = 4003, 4
     w, m, v = (torch.from_numpy(a) for a in _arrays(n, seed=6))
     _fake_ckpt(monkeypatch)
-    ck = sharded.ShardedCheckpointer(tmp_path, n, world)
+    ck = sharded.ShardedCheckpointer(tmp_path, n, world, pin_memory=False)
     staging = ck.staging
     assert staging.numel() == max(rcs.ckpt_bytes(k) for _, k in sharded.shard_ranges(n, world))
     for step in (1, 2, 3):
