@@ -481,6 +481,69 @@ def ceilings(torch, n: int, arrays=None, reps: int = 10) -> dict:
             "pattern_4r3w_us": k * 1e6}
 
 
+VIEW_OFFSETS = [(0, 0, 0, 0), (0, 1, 0, 0), (0, 0, 1, 0), (0, 0, 0, 1), (1, 0, 0, 0),
+                (1, 2, 0, 0), (0, 1, 2, 3), (2, 0, 1, 3), (1, 1, 1, 1), (0, 0, 0, 4)]
+
+
+def views_leg(torch, rcs, wl, steps: int, rounds: int = 3) -> dict:
+    """The step on views of w, g, m, v at several element offsets (so at
+    several 16- and 256-byte phases), with the buffers' physical placement
+    held fixed: one set of padded buffers per round, every offset case timed
+    on views into the same buffers, interleaved; mean us/step per case."""
+    n = wl.n
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = {offs: [] for offs in VIEW_OFFSETS}
+    for _ in range(rounds):
+        bufs = [torch.zeros(n + 128, device="cuda") for _ in range(4)]
+        bufs[0].normal_(0.0, 0.02)
+        bufs[1].normal_(0.0, wl.grad_sigma)
+        for offs in VIEW_OFFSETS:
+            w, g, m, v = (b[o:o + n] for b, o in zip(bufs, offs))
+            for t in range(1, 4):
+                rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip, stream=stream)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for t in range(4, 4 + steps):
+                rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[offs].append(e0.elapsed_time(e1) / steps * 1e3)
+        del bufs
+        torch.cuda.empty_cache()
+    base = sum(times[(0, 0, 0, 0)]) / rounds
+
+    # the asynchronous pack's snapshot kernel at the same size: n % 4 == 0 with
+    # everything aligned, n % 4 == 3 (the m and v parts off a 16-byte
+    # boundary), and a snapshot buffer one float off (every source shifted)
+    snaps = {}
+    W, M, V = (torch.zeros(n + 4, device="cuda") for _ in range(3))
+    S = torch.empty(3 * n + 8, device="cuda")
+    host = torch.empty(rcs.ckpt_bytes(n), dtype=torch.uint8, pin_memory=True)
+    copy_stream = torch.cuda.Stream()
+    for label, nn, so in (("n%4=0", n, 0), ("n%4=3", n - 1, 0), ("snapshot+1", n, 1)):
+        w, m, v, snap = W[:nn], M[:nn], V[:nn], S[so:so + 3 * nn]
+        buf = host[:rcs.ckpt_bytes(nn)]
+        ts = []
+        for _ in range(4):
+            e0.record(stream)
+            rcs.ckpt_pack_async(0, w, m, v, snap, buf, compute_stream=stream,
+                                copy_stream=copy_stream)
+            e1.record(stream)
+            rcs.ckpt_pack_wait(snap)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        snaps[label] = sorted(ts[1:])[1]  # median of the last three
+    del W, M, V, S, host
+    torch.cuda.empty_cache()
+    return {"n": n, "steps": steps, "rounds": rounds, "snapshot_us": snaps,
+            "us_per_step": {",".join(map(str, o)): sum(t) / rounds for o, t in times.items()},
+            "vs_aligned": {",".join(map(str, o)): sum(t) / rounds / base - 1
+                           for o, t in times.items()},
+            "what": "offsets of w, g, m, v in elements past 512-byte aligned buffers; "
+                    "mean over rounds of fresh buffers, all cases on the same buffers per round"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,6 +559,8 @@ def main() -> int:
                     help="oracle time budget per other workload")
     ap.add_argument("--no-torch-ref", action="store_true",
                     help="skip timing PyTorch's fused AdamW + clip on the same inputs")
+    ap.add_argument("--views", action="store_true",
+                    help="only time the step on views at several element offsets (fixed placement)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -525,6 +590,10 @@ def main() -> int:
     wl = workloads.WORKLOADS[args.workload]
     n = wl.n
     dev = torch.device("cuda:0")
+    if args.views:
+        rcs.lib()
+        print(json.dumps({"views": views_leg(torch, rcs, wl, args.steps)}), flush=True)
+        return 0
     rcs.lib()
     _log(f"[bench] workload {wl.name} n={n:,}: generating inputs on the device")
     w = workloads.init_params(wl, device=dev)
