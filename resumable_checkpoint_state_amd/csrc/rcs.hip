@@ -395,6 +395,18 @@ __device__ __forceinline__ void st_shifted(float *__restrict__ xb, int q, int64_
     }
 }
 
+// The chunk of the vectors block blockIdx.x works on: a bijection of
+// [0, gridDim.x) that puts block b in contiguous region b % kRegions, at
+// position b / kRegions. Blocks are dispatched round-robin over the XCDs, so
+// each XCD streams its own regions, and neighbouring chunks (which share a
+// cache line at their common edge when an array is off the body's phase) run
+// on the same XCD and its L2.
+__device__ __forceinline__ int64_t chunk_of_block() {
+    const int64_t nblk = gridDim.x, b = blockIdx.x;
+    const int64_t k = kRegions, q = nblk / k, r = nblk % k, x = b % k, j = b / k;
+    return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
 // Phases of w, g, m, v relative to the 16-byte aligned body, in floats
 // (0 = at the body's phase).
 struct Phases {
@@ -446,13 +458,7 @@ __device__ __forceinline__ void update_body(float *__restrict__ wf, const float 
                                             float clip, ClipScalars *__restrict__ sc,
                                             const StepScalars &h, double *lds) {
     const int64_t n4 = n >> 2;
-    int64_t c = blockIdx.x;
-    {  // bijection of [0, nblk): region b % k, position b / k
-        const int64_t nblk = gridDim.x;
-        const int64_t k = kRegions, q = nblk / k, r = nblk % k, x = c % k, j = c / k;
-        c = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
-    }
-    const int64_t i = c * kUpdThreads + threadIdx.x;
+    const int64_t i = chunk_of_block() * kUpdThreads + threadIdx.x;
     double xp[kPartsPerLane];
     if constexpr (FOLD) load_partials(partials, nparts, xp);
     const int64_t ic = i < n4 ? i : n4 - 1;
@@ -655,19 +661,25 @@ __global__ __launch_bounds__(256) void grad_scale_scalar(float *__restrict__ g, 
 // the step file's payload [w | m | v], so that the training stream can keep
 // updating w, m, v while the snapshot drains to the host on a copy stream.
 // blockIdx.y picks the array (w, m, v) and its place snap + y n. Each part is
-// written in aligned 16-byte vectors from its first 16-byte boundary on
-// (block 0 also copies the 0-3 elements before that boundary and the 0-3
-// after the last vector). A source at another 16-byte phase than its
-// destination (an n not divisible by 4 puts the m and v parts there, and so
-// can a view) is read in aligned 16-byte vectors shifted across lanes, as the
-// update reads g, m, v at another phase than w (ld_shifted); ph holds that
-// phase in floats for each part. One vector per lane, one wave per block: 452-463 us against
-// 466-483 us with 256 lanes for the 1.49 GB snapshot at the ANDREA-120M size.
-// The host guarantees n >= 4 and 4-byte aligned pointers.
+// written in aligned 16-byte vectors from its next 256-byte boundary on
+// (ph.h*: the 0-63 elements before it, or 0-3 to the next 16-byte boundary
+// when fewer than 4 would follow; block 0 copies those one per lane, and the
+// 0-3 after the last vector), so its waves write whole cache lines (with the
+// snapshot buffer one float off a 16-byte boundary: 507-509 us at the
+// ANDREA-120M size, against 534 with 16-byte heads). A source at another
+// 16-byte phase than its destination (an n not divisible by 4 puts the m and
+// v parts there, and so can a view) is read in aligned 16-byte vectors
+// shifted across lanes, as the update reads arrays off the anchor's phase
+// (ld_shifted); ph.q* is that phase in floats. One vector per lane, one wave
+// per block (452-463 us against 466-483 us with 256 lanes for the 1.49 GB
+// snapshot at the ANDREA-120M size), blocks in address order (the update's
+// XCD region mapping measured no better here). The host guarantees a head
+// for every part and 4-byte aligned pointers.
 constexpr int kSnapThreads = 64;
-static_assert(kSnapThreads == kWave, "the shifted loads assume one wave per block");
+static_assert(kSnapThreads == kWave, "the shifted loads and the 0-63 element heads assume one wave");
 struct SnapPhases {
-    int w, m, v;
+    int qw, qm, qv;  // source phase relative to the destination's body, floats
+    int hw, hm, hv;  // elements before the destination's body
 };
 __global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *__restrict__ w,
                                                                   const float *__restrict__ m,
@@ -677,8 +689,8 @@ __global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *_
     const int y = blockIdx.y;
     const float *src = y == 0 ? w : y == 1 ? m : v;
     float *dst = snap + (int64_t)y * n;
-    const int head = (int)(((16u - (reinterpret_cast<uintptr_t>(dst) & 15u)) & 15u) >> 2);
-    const int q = y == 0 ? ph.w : y == 1 ? ph.m : ph.v;
+    const int q = y == 0 ? ph.qw : y == 1 ? ph.qm : ph.qv;
+    const int head = y == 0 ? ph.hw : y == 1 ? ph.hm : ph.hv;
     const int64_t nb = n - head;
     const int64_t nb4 = nb >> 2;
     const int64_t i = (int64_t)blockIdx.x * kSnapThreads + threadIdx.x;
@@ -686,13 +698,14 @@ __global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *_
         const int64_t ic = i < nb4 ? i : nb4 - 1;
         const float *sb = src + head;
         f32x4 x;
-        if (q == 0) x = ld_stream(reinterpret_cast<const f32x4 *>(sb) + ic);
+        if (q == 0)
+            x = ld_stream(reinterpret_cast<const f32x4 *>(sb) + ic);
         else
             x = ld_shifted(sb, q, ic, ic == 0 && head < q,
                            threadIdx.x == kWave - 1 || ic == nb4 - 1);
         if (i < nb4) st_stream(reinterpret_cast<f32x4 *>(dst + head) + i, x);
     }
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == 0) {  // each part's head and tail
         if ((int)threadIdx.x < head) dst[threadIdx.x] = src[threadIdx.x];
         if ((int)threadIdx.x < (int)(nb & 3)) {
             const int64_t k = head + (nb4 << 2) + threadIdx.x;
@@ -701,7 +714,8 @@ __global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *_
     }
 }
 
-// The same copy for pointers off a 4-byte boundary or n < 4.
+// The same copy for pointers off a 4-byte boundary, or parts too short for
+// a head and one vector.
 __global__ __launch_bounds__(256) void ckpt_snapshot_scalar(const float *__restrict__ w,
                                                             const float *__restrict__ m,
                                                             const float *__restrict__ v,
@@ -1376,17 +1390,23 @@ int ckpt_pack_async(int32_t step, int64_t n, const float *w, const float *m, con
     }
     if (pending && hipStreamWaitEvent(compute_stream, ss->copied, 0) != hipSuccess)
         return RCS_EHIP;
-    if (n >= 4 && aligned4(w) && aligned4(m) && aligned4(v) && aligned4(snapshot)) {
+    // each part's head (to its destination's next 256-byte boundary, or
+    // 16-byte one when fewer than 4 elements would follow) and its source's
+    // phase relative to the destination's body; the vector kernel needs a
+    // head for every part and 4-byte aligned sources
+    SnapPhases ph;
+    const float *src[3] = {w, m, v};
+    int *q[3] = {&ph.qw, &ph.qm, &ph.qv};
+    int *hd[3] = {&ph.hw, &ph.hm, &ph.hv};
+    bool vec = aligned4(w) && aligned4(m) && aligned4(v);
+    for (int k = 0; vec && k < 3; ++k) {
+        const int h = head_of(snapshot + (int64_t)k * n, n);
+        vec = h >= 0;
+        *hd[k] = h;
+        *q[k] = (int)(((reinterpret_cast<uintptr_t>(src[k]) + 4u * (uintptr_t)h) & 15u) >> 2);
+    }
+    if (vec) {
         const int64_t blocks = ((n >> 2) + kSnapThreads - 1) / kSnapThreads;  // one vector per lane
-        // each part's source phase relative to its destination's first 16-byte boundary
-        SnapPhases ph;
-        const float *src[3] = {w, m, v};
-        int *q[3] = {&ph.w, &ph.m, &ph.v};
-        for (int k = 0; k < 3; ++k) {
-            const uintptr_t d = reinterpret_cast<uintptr_t>(snapshot + (int64_t)k * n);
-            const uintptr_t head = ((16u - (d & 15u)) & 15u) >> 2;
-            *q[k] = (int)(((reinterpret_cast<uintptr_t>(src[k]) + 4u * head) & 15u) >> 2);
-        }
         hipLaunchKernelGGL(ckpt_snapshot_vec, dim3((unsigned)blocks, 3), dim3(kSnapThreads), 0,
                            compute_stream, w, m, v, snapshot, n, ph);
     } else {
