@@ -412,8 +412,12 @@ def config_leg(torch, rcs, workloads, name: str, steps: int, warmup: int,
            "description": wl.description}
     if host is not None:
         out["host_us_per_call"] = host
-    if name == "flat2e9":
-        out["ceilings"] = ceilings(torch, n, (w, grads[0], m, v))
+    # the streaming ceilings at this n on these buffers: at 2e9 the update's
+    # pattern rate without cache help, at the small sizes the per-launch floor
+    # of a kernel of the update's shape
+    out["ceilings"] = ceilings(torch, n, (w, grads[0], m, v))
+    out["update_vs_pattern_ceiling"] = (out["ceilings"]["pattern_4r3w_us"]
+                                        / meas["update_us"])
     del w, m, v, grads
     torch.cuda.empty_cache()
     if cpu_seconds is None:
@@ -434,12 +438,9 @@ def _ceiling_lib():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.rcs_ceiling_blocks.argtypes = [i64]
     L.rcs_ceiling_blocks.restype = i64
-    L.rcs_ceiling_read.argtypes = [vp, i64, vp, vp]
-    L.rcs_ceiling_read.restype = ctypes.c_int
-    L.rcs_ceiling_copy.argtypes = [vp, vp, i64, vp]
-    L.rcs_ceiling_copy.restype = ctypes.c_int
-    L.rcs_ceiling_4r3w.argtypes = [vp, vp, vp, vp, i64, vp]
-    L.rcs_ceiling_4r3w.restype = ctypes.c_int
+    L.rcs_ceiling_time.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, vp, ctypes.c_int, vp,
+                                   ctypes.POINTER(ctypes.c_double)]
+    L.rcs_ceiling_time.restype = ctypes.c_int
     return L
 
 
@@ -447,8 +448,12 @@ def ceilings(torch, n: int, arrays=None, reps: int = 10) -> dict:
     """What the chip's HBM gives three streaming patterns over float32[n]:
     a read (the norm pass's shape), a copy and the update's 4-read/3-write
     pattern with one add per element (both in the update's shape), each the
-    average of `reps` launches timed with events on the current stream.
-    `arrays` (w, g, m, v) are reused (and overwritten) when given."""
+    average of `reps` launches on the current stream, each stamped with its
+    own start and stop events (as the library stamps the update's launches),
+    so at small n they give the per-launch floor of each shape. `arrays` (w,
+    g, m, v) are reused (and overwritten) when given."""
+    import ctypes
+
     L = _ceiling_lib()
     n4 = n // 4
     made = arrays is None
@@ -457,22 +462,15 @@ def ceilings(torch, n: int, arrays=None, reps: int = 10) -> dict:
     p = [a.data_ptr() for a in arrays]
     out_buf = torch.empty(max(1, L.rcs_ceiling_blocks(n4)), device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def timed(fn):
-        for _ in range(2):
-            assert fn() == 0
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps / 1e3
+    def timed(kind):
+        us = ctypes.c_double(0.0)
+        rc = L.rcs_ceiling_time(kind, p[0], p[1], p[2], p[3], n4, out_buf.data_ptr(), reps, st,
+                                ctypes.byref(us))
+        assert rc == 0, f"rcs_ceiling_time({kind}) returned {rc}"
+        return us.value / 1e6
 
-    r = timed(lambda: L.rcs_ceiling_read(p[0], n4, out_buf.data_ptr(), st))
-    c = timed(lambda: L.rcs_ceiling_copy(p[0], p[1], n4, st))
-    k = timed(lambda: L.rcs_ceiling_4r3w(p[0], p[1], p[2], p[3], n4, st))
+    r, c, k = timed(0), timed(1), timed(2)
     if made:
         del arrays
         torch.cuda.empty_cache()
@@ -685,6 +683,7 @@ def main() -> int:
 
     # what the HBM gives the same streaming patterns at this size (fresh buffers)
     result["ceilings"] = ceilings(torch, n)
+    result["update_vs_pattern_ceiling"] = result["ceilings"]["pattern_4r3w_us"] / meas["update_us"]
 
     if not args.no_torch_ref:
         ref = torch_reference(torch, wl, w, grads, min(args.steps, 50))

@@ -4,25 +4,29 @@
 // the training path: they compute nothing of the method.
 //
 // Over float32 arrays of n4 16-byte vectors:
-//   rcs_ceiling_read:  reads a in the norm pass's shape (at most 256 blocks of
-//                      512 lanes, 4 streaming 16-byte loads in flight per
-//                      lane, grid-stride); each block writes one float (the
-//                      sum of everything it read, so no load is dropped or
-//                      narrowed): 16 B/vector.
+//   read:  reads g in the norm pass's shape (at most 256 blocks of 512 lanes,
+//          4 streaming 16-byte loads in flight per lane, grid-stride); each
+//          block writes one float (the sum of everything it read, so no load
+//          is dropped or narrowed): 16 B/vector.
 // and in the update's launch shape (one wave per block, one 16-byte vector of
 // each array per lane, streaming loads and stores, block b working in
 // contiguous region b % 8 of the vectors):
-//   rcs_ceiling_copy:  b = a: 32 B/vector.
-//   rcs_ceiling_4r3w:  reads w, g, m, v and writes w, m, v with one add per
-//                      element (w += g, m += g, v += g): the update's 28 B per
-//                      4 elements with trivial arithmetic.
-// Each returns 0 after a successful launch, -1 for bad arguments, -4 if the
-// launch failed. Pointers must be 16-byte aligned device memory holding n4
-// vectors (rcs_ceiling_read's `out`: one float per block, rcs_ceiling_blocks
-// of them).
+//   copy:  m = w: 32 B/vector.
+//   4r3w:  reads w, g, m, v and writes w, m, v with one add per element
+//          (w += g, m += g, v += g): the update's 28 B per 4 elements with
+//          trivial arithmetic.
+// rcs_ceiling_time launches one of them `reps` times, each launch stamped
+// with its own start and stop events (the stamps of the launch itself, as
+// the library's instrumented updates take them), and returns the average
+// duration: at large n the rate HBM gives the pattern, at small n the
+// per-launch floor of the shape. Pointers must be 16-byte aligned device
+// memory holding n4 vectors (the read's `out`: one float per block,
+// rcs_ceiling_blocks of them).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 namespace {
 
@@ -99,35 +103,66 @@ dim3 grid_of(int64_t n4) { return dim3((unsigned)((n4 + kLanes - 1) / kLanes)); 
 
 int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
+bool ok_n4(int64_t n4) { return n4 >= 1 && n4 <= ((int64_t)1 << 36); }
+
+// One launch of ceiling `kind` (0 read, 1 copy, 2 4r3w) between the events
+// start and stop (either may be null).
+void launch_kind(int kind, f32x4 *w, const f32x4 *g, f32x4 *m, f32x4 *v, int64_t n4, float *out,
+                 hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (kind == 0)
+        hipExtLaunchKernelGGL(ceiling_read, dim3((unsigned)read_blocks(n4)), dim3(kReadLanes), 0,
+                              stream, start, stop, 0, g, n4, out);
+    else if (kind == 1)
+        hipExtLaunchKernelGGL(ceiling_copy, grid_of(n4), dim3(kLanes), 0, stream, start, stop, 0,
+                              static_cast<const f32x4 *>(w), m, n4);
+    else
+        hipExtLaunchKernelGGL(ceiling_4r3w, grid_of(n4), dim3(kLanes), 0, stream, start, stop, 0,
+                              w, g, m, v, n4);
+}
+
 }  // namespace
 
 extern "C" {
 
-// Blocks of rcs_ceiling_read (and so floats of its output) for n4 vectors.
+// Blocks of the read ceiling (and so floats of its output) for n4 vectors.
 int64_t rcs_ceiling_blocks(int64_t n4) { return n4 < 1 ? 0 : read_blocks(n4); }
 
-int rcs_ceiling_read(const float *a, int64_t n4, float *out, hipStream_t stream) {
-    if (!ok16(a) || out == nullptr || n4 < 1 || n4 > ((int64_t)1 << 36)) return -1;
-    hipLaunchKernelGGL(ceiling_read, dim3((unsigned)read_blocks(n4)), dim3(kReadLanes), 0, stream,
-                       reinterpret_cast<const f32x4 *>(a), n4, out);
-    return launched();
-}
-
-int rcs_ceiling_copy(const float *a, float *b, int64_t n4, hipStream_t stream) {
-    if (!ok16(a) || !ok16(b) || n4 < 1 || n4 > ((int64_t)1 << 36)) return -1;
-    hipLaunchKernelGGL(ceiling_copy, grid_of(n4), dim3(kLanes), 0, stream,
-                       reinterpret_cast<const f32x4 *>(a), reinterpret_cast<f32x4 *>(b), n4);
-    return launched();
-}
-
-int rcs_ceiling_4r3w(float *w, const float *g, float *m, float *v, int64_t n4,
-                     hipStream_t stream) {
-    if (!ok16(w) || !ok16(g) || !ok16(m) || !ok16(v) || n4 < 1 || n4 > ((int64_t)1 << 36))
+// Average duration in microseconds of `reps` stamped launches of ceiling
+// `kind` over w, g, m, v (kind 0 reads g into out; kind 1 copies w to m;
+// kind 2 is the 4-read/3-write pattern), after two unstamped ones. Blocks
+// until they are done. Returns 0, -1 for bad arguments, -4 on a HIP error.
+int rcs_ceiling_time(int kind, float *w, const float *g, float *m, float *v, int64_t n4,
+                     float *out, int reps, hipStream_t stream, double *avg_us) {
+    if (kind < 0 || kind > 2 || !ok_n4(n4) || reps < 1 || reps > 1000 || avg_us == nullptr)
         return -1;
-    hipLaunchKernelGGL(ceiling_4r3w, grid_of(n4), dim3(kLanes), 0, stream,
-                       reinterpret_cast<f32x4 *>(w), reinterpret_cast<const f32x4 *>(g),
-                       reinterpret_cast<f32x4 *>(m), reinterpret_cast<f32x4 *>(v), n4);
-    return launched();
+    if (kind == 0 && (!ok16(g) || out == nullptr)) return -1;
+    if (kind == 1 && (!ok16(w) || !ok16(m))) return -1;
+    if (kind == 2 && (!ok16(w) || !ok16(g) || !ok16(m) || !ok16(v))) return -1;
+    f32x4 *w4 = reinterpret_cast<f32x4 *>(w), *m4 = reinterpret_cast<f32x4 *>(m);
+    f32x4 *v4 = reinterpret_cast<f32x4 *>(v);
+    const f32x4 *g4 = reinterpret_cast<const f32x4 *>(g);
+    std::vector<hipEvent_t> ev(2 * (size_t)reps, nullptr);
+    int rc = 0;
+    for (auto &e : ev)
+        if (hipEventCreate(&e) != hipSuccess) rc = -4;
+    if (rc == 0) {
+        for (int k = 0; k < 2; ++k) launch_kind(kind, w4, g4, m4, v4, n4, out, stream, nullptr, nullptr);
+        for (int k = 0; k < reps; ++k)
+            launch_kind(kind, w4, g4, m4, v4, n4, out, stream, ev[2 * k], ev[2 * k + 1]);
+        rc = launched();
+    }
+    double sum_ms = 0.0;
+    if (rc == 0 && hipEventSynchronize(ev[2 * (size_t)reps - 1]) != hipSuccess) rc = -4;
+    for (int k = 0; rc == 0 && k < reps; ++k) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]) != hipSuccess) rc = -4;
+        sum_ms += ms;
+    }
+    for (auto &e : ev)
+        if (e != nullptr) (void)hipEventDestroy(e);
+    if (rc == 0) *avg_us = sum_ms / reps * 1e3;
+    (void)hipGetLastError();
+    return rc;
 }
 
 }  // extern "C"

@@ -215,3 +215,37 @@ def test_unpack_header_decisions_match_the_oracle_on_random_buffers(L):
         assert out.value == -7, ctx
         seen[orc] += 1
     assert min(seen.values()) > 100, seen
+
+
+def test_ceilings_library_loads_and_rejects_bad_arguments():
+    """bench.py's streaming-ceiling library: built for gfx950, exports its two
+    calls, and refuses bad arguments before any HIP call (no GPU needed)."""
+    path = os.path.join(ROOT, "resumable_checkpoint_state_amd", "libceilings.so")
+    if not os.path.exists(path):
+        from resumable_checkpoint_state_amd import _build
+        _build.build_ceilings()
+    assert b"gfx950" in open(path, "rb").read()
+    C = ctypes.CDLL(path)
+    C.rcs_ceiling_blocks.argtypes = [ctypes.c_int64]
+    C.rcs_ceiling_blocks.restype = ctypes.c_int64
+    vp = ctypes.c_void_p
+    C.rcs_ceiling_time.argtypes = [ctypes.c_int, vp, vp, vp, vp, ctypes.c_int64, vp,
+                                   ctypes.c_int, vp, ctypes.POINTER(ctypes.c_double)]
+    C.rcs_ceiling_time.restype = ctypes.c_int
+    # the read's grid: one block per 2048 vectors, at most 256
+    assert [C.rcs_ceiling_blocks(k) for k in (0, 1, 2048, 2049, 1 << 30)] == [0, 1, 1, 2, 256]
+    us = ctypes.c_double(-1.0)
+    fake = 0x1000
+    bad = [(3, fake, fake, fake, fake, 16, fake, 10),   # no such kind
+           (-1, fake, fake, fake, fake, 16, fake, 10),
+           (2, fake, fake, fake, fake, 0, fake, 10),    # no vectors
+           (2, fake, fake, fake, fake, 16, fake, 0),    # no launches
+           (2, fake, fake, fake, fake, 16, fake, 1001),
+           (0, fake, fake + 4, fake, fake, 16, fake, 10),  # g off a 16-byte boundary
+           (0, fake, fake, fake, fake, 16, None, 10),   # no output for the read
+           (1, None, fake, fake, fake, 16, fake, 10),
+           (2, fake, fake, fake, fake + 8, 16, fake, 10)]
+    for args in bad:
+        assert C.rcs_ceiling_time(*args, None, ctypes.byref(us)) == -1, args
+    assert C.rcs_ceiling_time(2, fake, fake, fake, fake, 16, fake, 10, None, None) == -1
+    assert us.value == -1.0
