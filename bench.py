@@ -55,8 +55,9 @@ def kernel_source_hash(text: bytes | None = None) -> str:
     return hashlib.sha256(code).hexdigest()[:16]
 
 
-def pmc_summary_for(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"adamw_update_vec_{workload}_pmc.md")
+def pmc_summary_for(workload: str, n: int) -> str:
+    """The counter summary of the update kernel that runs at n for this workload."""
+    return os.path.join(ROOT, "profiles", f"{update_kernel_name(n)}_{workload}_pmc.md")
 
 
 def measured_traffic(path: str = PMC_SUMMARY):
@@ -407,7 +408,7 @@ def config_leg(torch, rcs, workloads, name: str, steps: int, warmup: int,
            "kernels_us": {"norm": meas["norm_us"], "adamw_update": meas["update_us"]},
            "roofline": {"bound": "hbm", "kernel": update_kernel_name(n), "achieved": achieved,
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                        "traffic": measured_traffic(pmc_summary_for(name)),
+                        "traffic": measured_traffic(pmc_summary_for(name, n)),
                         "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
            "description": wl.description}
     if host is not None:
@@ -654,7 +655,7 @@ def main() -> int:
         "step_us_p90": meas["p90_us"],
         "roofline": {"bound": "hbm", "kernel": update_kernel_name(n), "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(pmc_summary_for(wl.name)),
+                     "traffic": measured_traffic(pmc_summary_for(wl.name, n)),
                      "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
     }
 
