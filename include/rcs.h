@@ -109,8 +109,8 @@ int rcs_init(int device, hipStream_t stream);
  * and w at another; arrays at the anchor's 16-byte phase take aligned
  * vectors, the others aligned vectors shifted across neighbouring lanes
  * (so every array is still read and written 16 bytes at a time). Up to
- * n = 8,388,608 the update kernel
- * also does the final reduction itself, in grad_norm_final's order (two
+ * n = 8,388,608 the update kernel also does the final reduction itself, in
+ * grad_norm_final's order (two
  * launches instead of three; the same norm bits as grad_global_norm). Arrays
  * too short for a head and one vector take partial, final and a scalar
  * update kernel with the same arithmetic.
@@ -185,16 +185,18 @@ int grad_clip_inplace(float *g, int64_t n, float clip, hipStream_t stream);
  * so it must be cleared before the next step's first micro-batch; the
  * resume page's update order likewise starts with zeroing the gradients).
  * g: device float32[n], n 1 .. RCS_MAX_N; 4 bytes written per element, with
- * 16-byte stores (256-lane blocks) from g's next 256-byte boundary on. A kernel, not
- * a memset, so it may be captured into a graph. Asynchronous on stream.
+ * 16-byte stores (256-lane blocks) from g's next 256-byte boundary on. A
+ * kernel, not a memset, so it may be captured into a graph. Asynchronous on
+ * stream.
  */
 int grad_zero(float *g, int64_t n, hipStream_t stream);
 
 /*
  * Copies the pre-clip norm computed by the most recent adamw_clip_step,
- * adamw_clip_step_accum, grad_clip_inplace or grad_global_norm on this stream into norm_out (device or pinned host
- * float64), in stream order. The resume lesson records this norm before the
- * clip to detect numerical faults. RCS_EINVAL if nothing ran on the stream.
+ * adamw_clip_step_accum, grad_clip_inplace or grad_global_norm on this stream
+ * into norm_out (device or pinned host float64), in stream order. The resume
+ * lesson records this norm before the clip to detect numerical faults.
+ * RCS_EINVAL if nothing ran on the stream.
  */
 int last_grad_norm(hipStream_t stream, double *norm_out);
 
@@ -308,8 +310,9 @@ int rcs_signals_poll(void);
  * patterns: asynchronous, atomic, keep the newest K; the checkpoints page's
  * SIGTERM save, after which the caller waits and exits). The writer owns a
  * device snapshot (12 n bytes), two pinned host images (8 + 12 n bytes
- * each), a copy stream and one worker thread, all made by rcs_ckpt_writer_create on the
- * current device and freed by rcs_ckpt_writer_destroy. dir must exist (as
+ * each), a copy stream and one worker thread, all made by
+ * rcs_ckpt_writer_create on the current device and freed by
+ * rcs_ckpt_writer_destroy. dir must exist (as
  * for ckpt_file_write); a missing or unwritable one makes each write fail
  * with RCS_EIO.
  *
@@ -346,9 +349,9 @@ int rcs_ckpt_writer_destroy(rcs_ckpt_writer *writer);
  * stamp HIP events (start of grad_norm_partial, end of the last norm kernel
  * -- grad_norm_partial itself when the update kernel does the final
  * reduction --, start and end of the update kernel) on one call in `every`
- * (the first call after
- * enabling is recorded), up to max_records recorded calls. rcs_profile_read synchronizes those events and returns the
- * summed milliseconds and the number of recorded calls. Enabling (or
+ * (the first call after enabling is recorded), up to max_records recorded
+ * calls. rcs_profile_read synchronizes those events and returns the summed
+ * milliseconds and the number of recorded calls. Enabling (or
  * disabling) discards earlier records. Events are created here, not in the
  * recorded calls.
  */
