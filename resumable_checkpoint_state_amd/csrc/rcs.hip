@@ -1052,7 +1052,8 @@ int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float c
         a.ph.v = (int)(((va + hb) & 15u) >> 2);
         const int mask = (a.ph.w == 0 ? 8 : 0) | (a.ph.g == 0 ? 4 : 0) | (a.ph.m == 0 ? 2 : 0) |
                          (a.ph.v == 0 ? 1 : 0);
-        switch (mask) {  // the anchor is at phase 0, so w, m or v always is
+        // the anchor is at phase 0: w (bit 8), or m together with v (bits 2 and 1)
+        switch (mask) {
             case 15: launch_update<true, true, true, true>(a); break;
             case 14: launch_update<true, true, true, false>(a); break;
             case 13: launch_update<true, true, false, true>(a); break;
@@ -1062,10 +1063,8 @@ int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float c
             case 9: launch_update<true, false, false, true>(a); break;
             case 8: launch_update<true, false, false, false>(a); break;
             case 7: launch_update<false, true, true, true>(a); break;
-            case 6: launch_update<false, true, true, false>(a); break;
             case 3: launch_update<false, false, true, true>(a); break;
-            case 2: launch_update<false, false, true, false>(a); break;
-            default: return RCS_EINVAL;  // unreachable: the anchor's own phase is 0
+            default: return RCS_EINVAL;  // unreachable, as above
         }
     } else {
         const int rc = launch_norm(g, n, h.gscale, clip, ws, stream, ev);
