@@ -481,7 +481,8 @@ def ceilings(torch, n: int, arrays=None, reps: int = 10) -> dict:
 
 
 VIEW_OFFSETS = [(0, 0, 0, 0), (0, 1, 0, 0), (0, 0, 1, 0), (0, 0, 0, 1), (1, 0, 0, 0),
-                (1, 2, 0, 0), (0, 1, 2, 3), (2, 0, 1, 3), (1, 1, 1, 1), (0, 0, 0, 4)]
+                (1, 2, 0, 0), (0, 1, 2, 3), (2, 0, 1, 3), (1, 1, 1, 1), (0, 0, 0, 4),
+                (4, 0, 0, 0), (0, 0, 4, 4)]
 
 
 def views_leg(torch, rcs, wl, steps: int, rounds: int = 3) -> dict:

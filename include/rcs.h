@@ -105,15 +105,17 @@ int rcs_init(int device, hipStream_t stream);
  * The update kernel streams the arrays in 16-byte vectors from the next
  * 256-byte boundary of an anchor array on and takes the 0-63 elements before
  * it separately (with fewer than 4 elements after that boundary: from the next
- * 16-byte one). The anchor is w, or m when m and v lie at one 16-byte phase
- * and w at another; arrays at the anchor's 16-byte phase take aligned
- * vectors, the others aligned vectors shifted across neighbouring lanes
- * (so every array is still read and written 16 bytes at a time). Up to
- * n = 8,388,608 the update kernel also does the final reduction itself, in
- * grad_norm_final's order (two
- * launches instead of three; the same norm bits as grad_global_norm). Arrays
- * too short for a head and one vector take partial, final and a scalar
- * update kernel with the same arithmetic.
+ * 16-byte one). The anchor is w or m, whichever shares its 128-byte line
+ * phase with more of w, m, v (m only when v lies at m's 16-byte phase; w on
+ * a tie); arrays at the anchor's 16-byte phase take aligned vectors, the
+ * others aligned vectors shifted across neighbouring lanes (so every array
+ * is still read and written 16 bytes at a time), and the lines that two
+ * waves share when an array's span does not start on a line are read and
+ * written with cache-retaining accesses. Up to n = 8,388,608 the update
+ * kernel also does the final reduction itself, in grad_norm_final's order
+ * (two launches instead of three; the same norm bits as grad_global_norm).
+ * Arrays too short for a head and one vector take partial, final and a
+ * scalar update kernel with the same arithmetic.
  */
 int adamw_clip_step(float *w, const float *g, float *m, float *v, int64_t n, int32_t t,
                     float lr, float wd, float clip, hipStream_t stream);

@@ -40,11 +40,13 @@
 //     same bits) and the step is two launches instead of three.
 //   * Arrays that start off a 16-byte boundary (views into a flat buffer)
 //     keep the vector kernels: block 0 takes the 0-63 elements before the
-//     anchor array's next 256-byte boundary one per lane (the anchor is w, or
-//     m when m and v share a 16-byte phase that w does not), and the waves
-//     stream whole cache lines from there; an array at another 16-byte phase
-//     is still read and written in aligned 16-byte vectors, shifted by whole
-//     floats across neighbouring lanes (adamw_update_mixed).
+//     anchor array's next 256-byte boundary one per lane (the anchor is w or
+//     m, whichever shares its line phase with more of the written arrays),
+//     and the waves stream whole cache lines from there; an array at another
+//     16-byte phase is still read and written in aligned 16-byte vectors,
+//     shifted by whole floats across neighbouring lanes (adamw_update_mixed).
+//     The lines a wave shares with its neighbour (an array whose span does not
+//     start on a line) are read and written with cache-retaining accesses.
 // No MFMA: nothing here is a contraction.
 //
 // Floating-point contract: built with -ffp-contract=off (and the pragma
@@ -313,6 +315,51 @@ __device__ __forceinline__ void st_stream(T *p, T x) {
     __builtin_nontemporal_store(x, p);
 }
 
+// Cache-retaining accesses for the 128-byte lines a wave shares with a
+// neighbouring wave. A wave's span of one array is 1 KiB from the vector its
+// lane 0 handles; when that array's span does not start on a line boundary,
+// its first and last lines are read and written by two waves. Streaming
+// accesses there make each wave fetch the whole line and write its part of
+// it on its own; these loads and stores (relaxed workgroup-scope atomics of 8
+// or 4 bytes, which the compiler emits as ordinary loads and stores with the
+// sc0 cache policy, no ordering implied) keep the line in L2, so the second
+// wave's read hits it and the two parts meet there. The neighbouring waves
+// run on the same XCD (one region per XCD). Measured at the ANDREA-120M size,
+// same buffers, one process: w 16 bytes past the others (so g, m and v
+// 112 bytes into a line) 721 us/step streaming, 627 with these and the anchor
+// chosen by line phase; v alone 16 bytes off 641 against 625; a 616-621 us
+// aligned step.
+__device__ __forceinline__ f32x4 ld_keep(const f32x4 *p) {
+    uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<f32x4 *>(p));
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
+__device__ __forceinline__ float ld_keep1(const float *p) {
+    uint32_t *q = reinterpret_cast<uint32_t *>(const_cast<float *>(p));
+    return __uint_as_float(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+
+__device__ __forceinline__ void st_keep(f32x4 *p, f32x4 x) {
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    const uint64_t a = (uint64_t)__float_as_uint(x.x) | ((uint64_t)__float_as_uint(x.y) << 32);
+    const uint64_t b = (uint64_t)__float_as_uint(x.z) | ((uint64_t)__float_as_uint(x.w) << 32);
+    __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Whether the 16-byte vector at p lies in a line its wave shares with a
+// neighbouring wave. a0: the vector the wave's lane 0 handles in the same
+// array. split: the array is read in shifted vectors, so the vector at a0 is
+// split between two waves whatever its line phase.
+__device__ __forceinline__ bool shared_line(const void *p, const void *a0, bool split) {
+    const uintptr_t l = reinterpret_cast<uintptr_t>(p) >> 7;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(a0);
+    return (split || (s & 127u) != 0) && (l == (s >> 7) || l == ((s + 1024u) >> 7));
+}
+
 // An array at another 16-byte phase than the anchor (the array whose body
 // starts on the 256-byte boundary): its body xb (the element matching the
 // anchor's first body element) lies q = 1-3 floats past a 16-byte boundary,
@@ -340,20 +387,22 @@ __device__ __forceinline__ f32x4 ld_shifted(const float *__restrict__ xb, int q,
     f32x4 a;
     if (first) {
         a = f32x4{0.f, 0.f, 0.f, 0.f};
-        a.w = ld_stream(xb + 3 - q);
-        if (q <= 2) a.z = ld_stream(xb + 2 - q);
-        if (q == 1) a.y = ld_stream(xb);
+        a.w = ld_keep1(xb + 3 - q);
+        if (q <= 2) a.z = ld_keep1(xb + 2 - q);
+        if (q == 1) a.y = ld_keep1(xb);
     } else {
-        a = ld_stream(reinterpret_cast<const f32x4 *>(xb - q) + ic);
+        const f32x4 *base = reinterpret_cast<const f32x4 *>(xb - q);
+        const int64_t i0 = ic - (int64_t)(threadIdx.x & (kWave - 1));
+        a = shared_line(base + ic, base + i0, true) ? ld_keep(base + ic) : ld_stream(base + ic);
     }
     float b0 = __shfl_down(a.x, 1, kWave);
     float b1 = __shfl_down(a.y, 1, kWave);
     float b2 = __shfl_down(a.z, 1, kWave);
     if (own) {
         const float *p = xb + 4 * ic + 4 - q;
-        b0 = ld_stream(p);
-        if (q >= 2) b1 = ld_stream(p + 1);
-        if (q == 3) b2 = ld_stream(p + 2);
+        b0 = ld_keep1(p);
+        if (q >= 2) b1 = ld_keep1(p + 1);
+        if (q == 3) b2 = ld_keep1(p + 2);
     }
     return q == 1 ? f32x4{a.y, a.z, a.w, b0} : q == 2 ? f32x4{a.z, a.w, b0, b1}
                                                      : f32x4{a.w, b0, b1, b2};
@@ -418,15 +467,25 @@ struct Phases {
 template <bool VEC>
 __device__ __forceinline__ f32x4 load4(const float *__restrict__ xb, int q, int64_t ic,
                                        int head, bool own) {
-    if constexpr (VEC) return ld_stream(reinterpret_cast<const f32x4 *>(xb) + ic);
-    else return ld_shifted(xb, q, ic, ic == 0 && head < q, own);
+    if constexpr (VEC) {
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(xb);
+        const int64_t i0 = ic - (int64_t)(threadIdx.x & (kWave - 1));
+        return shared_line(x4 + ic, x4 + i0, false) ? ld_keep(x4 + ic) : ld_stream(x4 + ic);
+    } else {
+        return ld_shifted(xb, q, ic, ic == 0 && head < q, own);
+    }
 }
 
 template <bool VEC>
 __device__ __forceinline__ void store4(float *__restrict__ xb, int q, int64_t i, f32x4 r,
                                        bool active, bool lane0, bool own) {
     if constexpr (VEC) {
-        if (active) st_stream(reinterpret_cast<f32x4 *>(xb) + i, r);
+        if (active) {
+            f32x4 *x4 = reinterpret_cast<f32x4 *>(xb);
+            const int64_t i0 = i - (int64_t)(threadIdx.x & (kWave - 1));
+            if (shared_line(x4 + i, x4 + i0, false)) st_keep(x4 + i, r);
+            else st_stream(x4 + i, r);
+        }
     } else {
         st_shifted(xb, q, i, r, active, lane0, own);
     }
@@ -446,8 +505,8 @@ __device__ __forceinline__ void store4(float *__restrict__ xb, int q, int64_t i,
 // wave per block: 529.7 against 552.2 us for the update at the ANDREA-120M
 // size, measured in one process).
 // w, g, m, v point `head` (0-63) elements past the arrays' starts, where the
-// body begins; the anchor array among w, m, v (the host's choice) has its body
-// on a 16-byte (normally 256-byte) boundary, and WV, GV, MV, VV say which
+// body begins; the anchor array (w or m, the host's choice) has its body on a
+// 16-byte (normally 256-byte) boundary, and WV, GV, MV, VV say which
 // arrays share its 16-byte phase (aligned vectors) rather than lying ph.*
 // floats past it (shifted vectors; kUpdThreads is one wave).
 template <bool FOLD, bool WV, bool GV, bool MV, bool VV>
@@ -993,13 +1052,27 @@ void launch_update(const UpdateLaunch &a) {
     }
 }
 
-// The anchor of the update's body among the written arrays w, m, v: the one
-// whose 16-byte phase the most of them share (w unless m and v share a phase
-// that w does not), so that as few written arrays as possible take shifted
-// vectors. 0 = w, 1 = m, 2 = v.
+// The anchor of the update's body among the written arrays w and m: each
+// scores 2 for every written array (w, m, v) at its 128-byte line phase and 1
+// for every one at its 16-byte phase, and the higher score wins (w on a tie).
+// Arrays at the anchor's line phase stream whole lines; at its 16-byte phase
+// only, they take aligned vectors with shared edge lines; otherwise shifted
+// vectors. m wins only when v shares its 16-byte phase (its score can exceed
+// w's only through v), so the anchor's phase always holds w, or m and v.
+// 0 = w, 1 = m.
 int anchor_of(uintptr_t wa, uintptr_t ma, uintptr_t va) {
-    const uintptr_t pw = wa & 15u, pm = ma & 15u, pv = va & 15u;
-    return (pm == pv && pw != pm) ? 1 : 0;
+    const uintptr_t o[3] = {wa & 127u, ma & 127u, va & 127u};
+    int best = 0, best_score = -1;
+    for (int a = 0; a < 2; ++a) {
+        int score = 0;
+        for (int x = 0; x < 3; ++x)
+            score += (o[x] == o[a] ? 2 : 0) + ((o[x] & 15u) == (o[a] & 15u) ? 1 : 0);
+        if (score > best_score) {
+            best = a;
+            best_score = score;
+        }
+    }
+    return best;
 }
 
 // The whole step a1..a3. Vector form (all four arrays 4-byte aligned, at

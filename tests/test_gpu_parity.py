@@ -194,8 +194,11 @@ def test_update_parity_ragged_sizes(dev, n):
 # differs from the anchor's modulo 4 (the anchor is w, or m when m and v share
 # a phase w does not) take shifted 16-byte vectors in the vector kernels
 # (adamw_update_mixed: every reachable combination appears here, in both
-# final-reduction forms). Views too short for either head take the scalar
-# kernels.
+# final-reduction forms). The anchor is w or m, whichever shares its 128-byte
+# line phase with more of the written arrays (m only when v shares its 16-byte
+# phase); arrays at the anchor's 16-byte but another line phase take aligned
+# vectors with cache-retaining accesses on the lines two waves share. Views
+# too short for either head take the scalar kernels.
 UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3), 50_001),
                    ((1, 1, 1, 1), 67), ((1, 1, 1, 1), 70), ((2, 2, 2, 2), 66),
                    ((3, 3, 3, 3), 5), ((3, 3, 3, 3), 6), ((1, 1, 1, 1), 7), ((2, 2, 2, 2), 9),
@@ -212,7 +215,14 @@ UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3)
                    ((1, 2, 0, 0), 50_001), ((1, 2, 0, 0), 12_800_003), ((1, 0, 0, 0), 8_388_611),
                    ((1, 0, 0, 0), 6), ((2, 0, 0, 0), 5), ((0, 1, 2, 0), 4099),
                    ((0, 0, 0, 1), 12_800_003), ((1, 1, 0, 2), 8_388_611),
-                   ((1, 0, 1, 2), 12_800_003), ((0, 1, 2, 3), 12_800_003)]
+                   ((1, 0, 1, 2), 12_800_003), ((0, 1, 2, 3), 12_800_003),
+                   # line phases: w 16 bytes past the others (anchored on m), the
+                   # written arrays split 2 + 1 or 1 + 1 + 1 over line phases, g
+                   # alone off them, with fold and without, ragged tails
+                   ((4, 0, 0, 0), 50_001), ((4, 0, 0, 0), 12_800_003), ((4, 4, 0, 0), 8_388_611),
+                   ((0, 0, 4, 4), 8_388_608), ((0, 0, 0, 4), 12_800_003), ((0, 4, 0, 0), 4099),
+                   ((8, 0, 4, 12), 50_001), ((0, 0, 28, 28), 70), ((28, 0, 0, 0), 66),
+                   ((5, 1, 1, 1), 50_001), ((1, 5, 2, 2), 12_800_003), ((4, 0, 0, 1), 8_388_611)]
 
 
 @pytest.mark.parametrize("offs,n", UNALIGNED_CASES)
