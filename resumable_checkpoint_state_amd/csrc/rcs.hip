@@ -376,33 +376,45 @@ __device__ __forceinline__ bool shared_line(const void *p, const void *a0, bool 
 // read by itself or by the next lane of its own wave before that wave's
 // stores; other waves only ever write positions this lane discards.
 
+template <bool KEEP>
+__device__ __forceinline__ float ld_edge1(const float *p) {
+    if constexpr (KEEP) return ld_keep1(p);
+    else return ld_stream(p);
+}
+
 // xb[4i .. 4i+3] for vector ic (i clamped to the body). first: ic is vector 0
 // and the aligned vector holding xb[0] starts before the array (head < q):
 // the lane's elements of it are read one by one. own: the next lane does not
 // hold the next aligned vector (this is the wave's last lane or the body's
-// last vector): positions 0..q-1 of it are read one by one. Every lane of the
+// last vector): positions 0..q-1 of it are read one by one. KEEP: the lines
+// shared with the neighbouring wave (always two: the vector at the wave's
+// start is split between the waves) are read with cache-retaining loads,
+// for the update, whose neighbouring waves run on one XCD; the snapshot
+// kernel, whose neighbouring blocks do not, streams them. Every lane of the
 // wave must call this (cross-lane shifts).
+template <bool KEEP>
 __device__ __forceinline__ f32x4 ld_shifted(const float *__restrict__ xb, int q, int64_t ic,
                                             bool first, bool own) {
     f32x4 a;
     if (first) {
         a = f32x4{0.f, 0.f, 0.f, 0.f};
-        a.w = ld_keep1(xb + 3 - q);
-        if (q <= 2) a.z = ld_keep1(xb + 2 - q);
-        if (q == 1) a.y = ld_keep1(xb);
+        a.w = ld_edge1<KEEP>(xb + 3 - q);
+        if (q <= 2) a.z = ld_edge1<KEEP>(xb + 2 - q);
+        if (q == 1) a.y = ld_edge1<KEEP>(xb);
     } else {
         const f32x4 *base = reinterpret_cast<const f32x4 *>(xb - q);
         const int64_t i0 = ic - (int64_t)(threadIdx.x & (kWave - 1));
-        a = shared_line(base + ic, base + i0, true) ? ld_keep(base + ic) : ld_stream(base + ic);
+        a = KEEP && shared_line(base + ic, base + i0, true) ? ld_keep(base + ic)
+                                                            : ld_stream(base + ic);
     }
     float b0 = __shfl_down(a.x, 1, kWave);
     float b1 = __shfl_down(a.y, 1, kWave);
     float b2 = __shfl_down(a.z, 1, kWave);
     if (own) {
         const float *p = xb + 4 * ic + 4 - q;
-        b0 = ld_keep1(p);
-        if (q >= 2) b1 = ld_keep1(p + 1);
-        if (q == 3) b2 = ld_keep1(p + 2);
+        b0 = ld_edge1<KEEP>(p);
+        if (q >= 2) b1 = ld_edge1<KEEP>(p + 1);
+        if (q == 3) b2 = ld_edge1<KEEP>(p + 2);
     }
     return q == 1 ? f32x4{a.y, a.z, a.w, b0} : q == 2 ? f32x4{a.z, a.w, b0, b1}
                                                      : f32x4{a.w, b0, b1, b2};
@@ -472,7 +484,7 @@ __device__ __forceinline__ f32x4 load4(const float *__restrict__ xb, int q, int6
         const int64_t i0 = ic - (int64_t)(threadIdx.x & (kWave - 1));
         return shared_line(x4 + ic, x4 + i0, false) ? ld_keep(x4 + ic) : ld_stream(x4 + ic);
     } else {
-        return ld_shifted(xb, q, ic, ic == 0 && head < q, own);
+        return ld_shifted<true>(xb, q, ic, ic == 0 && head < q, own);
     }
 }
 
@@ -760,8 +772,8 @@ __global__ __launch_bounds__(kSnapThreads) void ckpt_snapshot_vec(const float *_
         if (q == 0)
             x = ld_stream(reinterpret_cast<const f32x4 *>(sb) + ic);
         else
-            x = ld_shifted(sb, q, ic, ic == 0 && head < q,
-                           threadIdx.x == kWave - 1 || ic == nb4 - 1);
+            x = ld_shifted<false>(sb, q, ic, ic == 0 && head < q,
+                                  threadIdx.x == kWave - 1 || ic == nb4 - 1);
         if (i < nb4) st_stream(reinterpret_cast<f32x4 *>(dst + head) + i, x);
     }
     if (blockIdx.x == 0) {  // each part's head and tail
