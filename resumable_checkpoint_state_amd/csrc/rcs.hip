@@ -476,11 +476,14 @@ struct Phases {
 
 // Four elements of an array's body per lane: an aligned vector (VEC: the
 // array is at the body's 16-byte phase) or a shifted one.
-template <bool VEC>
+// LINES: some array's span may not start on a line (shared_line is checked);
+// false when every array's body starts on a line boundary.
+template <bool VEC, bool LINES>
 __device__ __forceinline__ f32x4 load4(const float *__restrict__ xb, int q, int64_t ic,
                                        int head, bool own) {
     if constexpr (VEC) {
         const f32x4 *x4 = reinterpret_cast<const f32x4 *>(xb);
+        if constexpr (!LINES) return ld_stream(x4 + ic);
         const int64_t i0 = ic - (int64_t)(threadIdx.x & (kWave - 1));
         return shared_line(x4 + ic, x4 + i0, false) ? ld_keep(x4 + ic) : ld_stream(x4 + ic);
     } else {
@@ -488,14 +491,14 @@ __device__ __forceinline__ f32x4 load4(const float *__restrict__ xb, int q, int6
     }
 }
 
-template <bool VEC>
+template <bool VEC, bool LINES>
 __device__ __forceinline__ void store4(float *__restrict__ xb, int q, int64_t i, f32x4 r,
                                        bool active, bool lane0, bool own) {
     if constexpr (VEC) {
         if (active) {
             f32x4 *x4 = reinterpret_cast<f32x4 *>(xb);
             const int64_t i0 = i - (int64_t)(threadIdx.x & (kWave - 1));
-            if (shared_line(x4 + i, x4 + i0, false)) st_keep(x4 + i, r);
+            if (LINES && shared_line(x4 + i, x4 + i0, false)) st_keep(x4 + i, r);
             else st_stream(x4 + i, r);
         }
     } else {
@@ -520,8 +523,9 @@ __device__ __forceinline__ void store4(float *__restrict__ xb, int q, int64_t i,
 // body begins; the anchor array (w or m, the host's choice) has its body on a
 // 16-byte (normally 256-byte) boundary, and WV, GV, MV, VV say which
 // arrays share its 16-byte phase (aligned vectors) rather than lying ph.*
-// floats past it (shifted vectors; kUpdThreads is one wave).
-template <bool FOLD, bool WV, bool GV, bool MV, bool VV>
+// floats past it (shifted vectors; kUpdThreads is one wave). LINES as for
+// load4 (always true when an array is shifted).
+template <bool FOLD, bool LINES, bool WV, bool GV, bool MV, bool VV>
 __device__ __forceinline__ void update_body(float *__restrict__ wf, const float *__restrict__ gf,
                                             float *__restrict__ mf, float *__restrict__ vf,
                                             int64_t n, int head, Phases ph,
@@ -535,10 +539,10 @@ __device__ __forceinline__ void update_body(float *__restrict__ wf, const float 
     const int64_t ic = i < n4 ? i : n4 - 1;
     const int lane = (int)threadIdx.x & (kWave - 1);
     const bool own = lane == kWave - 1 || ic == n4 - 1;
-    f32x4 gr = load4<GV>(gf, ph.g, ic, head, own);
-    f32x4 wr = load4<WV>(wf, ph.w, ic, head, own);
-    f32x4 mr = load4<MV>(mf, ph.m, ic, head, own);
-    f32x4 vr = load4<VV>(vf, ph.v, ic, head, own);
+    f32x4 gr = load4<GV, LINES>(gf, ph.g, ic, head, own);
+    f32x4 wr = load4<WV, LINES>(wf, ph.w, ic, head, own);
+    f32x4 mr = load4<MV, LINES>(mf, ph.m, ic, head, own);
+    f32x4 vr = load4<VV, LINES>(vf, ph.v, ic, head, own);
     ClipScalars cs;
     if constexpr (FOLD) {
         cs = final_reduce(xp, nparts, clip, lds);
@@ -551,9 +555,9 @@ __device__ __forceinline__ void update_body(float *__restrict__ wf, const float 
     const bool active = i < n4;
     if (active) adamw_vec4(wr, gr, mr, vr, s, h);
     const bool lane0 = lane == 0;
-    store4<WV>(wf, ph.w, i, wr, active, lane0, own);
-    store4<MV>(mf, ph.m, i, mr, active, lane0, own);
-    store4<VV>(vf, ph.v, i, vr, active, lane0, own);
+    store4<WV, LINES>(wf, ph.w, i, wr, active, lane0, own);
+    store4<MV, LINES>(mf, ph.m, i, mr, active, lane0, own);
+    store4<VV, LINES>(vf, ph.v, i, vr, active, lane0, own);
     // block 0: the head elements before the body (indices -head .. -1);
     // the last block: the n % 4 after the last vector
     if (blockIdx.x == 0 && (int)threadIdx.x < head) {
@@ -576,24 +580,27 @@ __device__ __forceinline__ void update_body(float *__restrict__ wf, const float 
 
 // a3 after grad_norm_final, all four arrays at one 16-byte phase. w, g, m, v
 // point `head` (0-63) elements past the arrays' starts, at 16-byte
-// boundaries; n counts from there.
+// boundaries; n counts from there. LINES: some array's body is not on a
+// 128-byte line boundary.
+template <bool LINES>
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec(
     float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
     float *__restrict__ v, int64_t n, int head, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false, true, true, true, true>(w, g, m, v, n, head, Phases{0, 0, 0, 0}, nullptr,
-                                               0, 0.0f, const_cast<ClipScalars *>(sc), h,
-                                               nullptr);
+    update_body<false, LINES, true, true, true, true>(w, g, m, v, n, head, Phases{0, 0, 0, 0},
+                                                      nullptr, 0, 0.0f,
+                                                      const_cast<ClipScalars *>(sc), h, nullptr);
 }
 
 // a2 + a3 in one kernel (small n).
+template <bool LINES>
 __global__ __launch_bounds__(kUpdThreads) void adamw_update_vec_fold(
     float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
     float *__restrict__ v, int64_t n, int head, const double *__restrict__ partials, int nparts,
     float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true, true, true, true, true>(w, g, m, v, n, head, Phases{0, 0, 0, 0}, partials,
-                                              nparts, clip, sc_out, h, lds);
+    update_body<true, LINES, true, true, true, true>(w, g, m, v, n, head, Phases{0, 0, 0, 0},
+                                                     partials, nparts, clip, sc_out, h, lds);
 }
 
 // The same two kernels when the arrays lie at more than one 16-byte phase
@@ -605,8 +612,8 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_mixed(
     float *__restrict__ w, const float *__restrict__ g, float *__restrict__ m,
     float *__restrict__ v, int64_t n, int head, Phases ph, const ClipScalars *__restrict__ sc,
     StepScalars h) {
-    update_body<false, WV, GV, MV, VV>(w, g, m, v, n, head, ph, nullptr, 0, 0.0f,
-                                       const_cast<ClipScalars *>(sc), h, nullptr);
+    update_body<false, true, WV, GV, MV, VV>(w, g, m, v, n, head, ph, nullptr, 0, 0.0f,
+                                             const_cast<ClipScalars *>(sc), h, nullptr);
 }
 
 template <bool WV, bool GV, bool MV, bool VV>
@@ -615,8 +622,8 @@ __global__ __launch_bounds__(kUpdThreads) void adamw_update_mixed_fold(
     float *__restrict__ v, int64_t n, int head, Phases ph, const double *__restrict__ partials,
     int nparts, float clip, ClipScalars *__restrict__ sc_out, StepScalars h) {
     __shared__ double lds[kUpdThreads / kWave];
-    update_body<true, WV, GV, MV, VV>(w, g, m, v, n, head, ph, partials, nparts, clip, sc_out, h,
-                                      lds);
+    update_body<true, true, WV, GV, MV, VV>(w, g, m, v, n, head, ph, partials, nparts, clip,
+                                            sc_out, h, lds);
 }
 
 // a3 for arrays that are not 4-byte aligned or too short for a head and one
@@ -1032,6 +1039,7 @@ struct UpdateLaunch {
     int head;
     Phases ph;
     bool fold;
+    bool lines;  // some array's body does not start on a 128-byte line
     const double *partials;
     int nparts;
     float clip;
@@ -1045,13 +1053,22 @@ template <bool WV, bool GV, bool MV, bool VV>
 void launch_update(const UpdateLaunch &a) {
     const dim3 block(kUpdThreads);
     if constexpr (WV && GV && MV && VV) {
-        if (a.fold)
-            hipExtLaunchKernelGGL(adamw_update_vec_fold, a.grid, block, 0, a.stream, a.e2, a.e3, 0,
-                                  a.w, a.g, a.m, a.v, a.nb, a.head, a.partials, a.nparts, a.clip,
-                                  a.sc, a.h);
+        if (a.fold && a.lines)
+            hipExtLaunchKernelGGL(adamw_update_vec_fold<true>, a.grid, block, 0, a.stream, a.e2,
+                                  a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head, a.partials, a.nparts,
+                                  a.clip, a.sc, a.h);
+        else if (a.fold)
+            hipExtLaunchKernelGGL(adamw_update_vec_fold<false>, a.grid, block, 0, a.stream, a.e2,
+                                  a.e3, 0, a.w, a.g, a.m, a.v, a.nb, a.head, a.partials, a.nparts,
+                                  a.clip, a.sc, a.h);
+        else if (a.lines)
+            hipExtLaunchKernelGGL(adamw_update_vec<true>, a.grid, block, 0, a.stream, a.e2, a.e3,
+                                  0, a.w, a.g, a.m, a.v, a.nb, a.head, (const ClipScalars *)a.sc,
+                                  a.h);
         else
-            hipExtLaunchKernelGGL(adamw_update_vec, a.grid, block, 0, a.stream, a.e2, a.e3, 0, a.w,
-                                  a.g, a.m, a.v, a.nb, a.head, (const ClipScalars *)a.sc, a.h);
+            hipExtLaunchKernelGGL(adamw_update_vec<false>, a.grid, block, 0, a.stream, a.e2, a.e3,
+                                  0, a.w, a.g, a.m, a.v, a.nb, a.head, (const ClipScalars *)a.sc,
+                                  a.h);
     } else {
         if (a.fold)
             hipExtLaunchKernelGGL(adamw_update_mixed_fold<WV, GV, MV, VV>, a.grid, block, 0,
@@ -1121,6 +1138,7 @@ int launch_step(float *w, const float *g, float *m, float *v, int64_t n, float c
         a.v = v + head;
         a.head = head;
         a.fold = fold;
+        a.lines = (((uintptr_t)a.w | (uintptr_t)a.g | (uintptr_t)a.m | (uintptr_t)a.v) & 127u) != 0;
         a.partials = ws->partials;
         a.nparts = norm_blocks(n);
         a.clip = clip;
