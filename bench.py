@@ -490,10 +490,18 @@ def views_leg(torch, rcs, wl, steps: int, rounds: int = 3) -> dict:
     several 16- and 256-byte phases), with the buffers' physical placement
     held fixed: one set of padded buffers per round, every offset case timed
     on views into the same buffers, interleaved; mean us/step per case."""
+    import ctypes
+
     n = wl.n
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = {offs: [] for offs in VIEW_OFFSETS}
+    # the bare 4-read/3-write pattern on the same buffers: all arrays on a line,
+    # v 16 bytes past one with streaming accesses, and the same with
+    # cache-retaining accesses on the lines two waves share
+    lines = {"aligned": [], "v+16B_streaming": [], "v+16B_shared_lines_kept": []}
+    L = _ceiling_lib()
+    n4 = n // 4
     for _ in range(rounds):
         bufs = [torch.zeros(n + 128, device="cuda") for _ in range(4)]
         bufs[0].normal_(0.0, 0.02)
@@ -509,6 +517,14 @@ def views_leg(torch, rcs, wl, steps: int, rounds: int = 3) -> dict:
             e1.record(stream)
             torch.cuda.synchronize()
             times[offs].append(e0.elapsed_time(e1) / steps * 1e3)
+        p = [b.data_ptr() for b in bufs]
+        for label, kind, v_off in (("aligned", 2, 0), ("v+16B_streaming", 2, 16),
+                                   ("v+16B_shared_lines_kept", 3, 16)):
+            us = ctypes.c_double(0.0)
+            rc = L.rcs_ceiling_time(kind, p[0], p[1], p[2], p[3] + v_off, n4, None, 10,
+                                    stream.cuda_stream, ctypes.byref(us))
+            assert rc == 0, f"rcs_ceiling_time({kind}) returned {rc}"
+            lines[label].append(us.value)
         del bufs
         torch.cuda.empty_cache()
     base = sum(times[(0, 0, 0, 0)]) / rounds
@@ -537,6 +553,7 @@ def views_leg(torch, rcs, wl, steps: int, rounds: int = 3) -> dict:
     del W, M, V, S, host
     torch.cuda.empty_cache()
     return {"n": n, "steps": steps, "rounds": rounds, "snapshot_us": snaps,
+            "pattern_4r3w_us": {k: sum(t) / rounds for k, t in lines.items()},
             "us_per_step": {",".join(map(str, o)): sum(t) / rounds for o, t in times.items()},
             "vs_aligned": {",".join(map(str, o)): sum(t) / rounds / base - 1
                            for o, t in times.items()},

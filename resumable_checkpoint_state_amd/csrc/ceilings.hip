@@ -15,6 +15,11 @@
 //   4r3w:  reads w, g, m, v and writes w, m, v with one add per element
 //          (w += g, m += g, v += g): the update's 28 B per 4 elements with
 //          trivial arithmetic.
+//   4r3w_keep: the same, but vectors in a 128-byte line the wave shares with
+//          a neighbouring wave (an array whose span does not start on a
+//          line) are loaded and stored with the sc0 cache policy (relaxed
+//          workgroup-scope atomics), as the update does for views; with every
+//          array on a line it is 4r3w.
 // rcs_ceiling_time launches one of them `reps` times, each launch stamped
 // with its own start and stop events (the stamps of the launch itself, as
 // the library's instrumented updates take them), and returns the average
@@ -97,6 +102,52 @@ __global__ __launch_bounds__(kLanes) void ceiling_4r3w(f32x4 *__restrict__ w,
     }
 }
 
+// Whether the vector at p lies in a line the wave shares with a neighbour;
+// a0 is the vector of the wave's lane 0 in the same array.
+__device__ __forceinline__ bool shared_line(const void *p, const void *a0) {
+    const uintptr_t l = reinterpret_cast<uintptr_t>(p) >> 7;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(a0);
+    return (s & 127u) != 0 && (l == (s >> 7) || l == ((s + 1024u) >> 7));
+}
+
+__device__ __forceinline__ f32x4 ld_line(const f32x4 *p, const f32x4 *a0) {
+    if (!shared_line(p, a0)) return __builtin_nontemporal_load(p);
+    uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<f32x4 *>(p));
+    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
+__device__ __forceinline__ void st_line(f32x4 *p, const f32x4 *a0, f32x4 x) {
+    if (!shared_line(p, a0)) {
+        __builtin_nontemporal_store(x, p);
+        return;
+    }
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    __hip_atomic_store(q, (uint64_t)__float_as_uint(x.x) | ((uint64_t)__float_as_uint(x.y) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(x.z) | ((uint64_t)__float_as_uint(x.w) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__global__ __launch_bounds__(kLanes) void ceiling_4r3w_keep(f32x4 *__restrict__ w,
+                                                            const f32x4 *__restrict__ g,
+                                                            f32x4 *__restrict__ m,
+                                                            f32x4 *__restrict__ v, int64_t n4) {
+    const int64_t c = chunk_of_block() * kLanes;
+    const int64_t i = c + threadIdx.x;
+    if (i < n4) {
+        const f32x4 gg = ld_line(g + i, g + c);
+        const f32x4 ww = ld_line(w + i, w + c);
+        const f32x4 mm = ld_line(m + i, m + c);
+        const f32x4 vv = ld_line(v + i, v + c);
+        st_line(w + i, w + c, ww + gg);
+        st_line(m + i, m + c, mm + gg);
+        st_line(v + i, v + c, vv + gg);
+    }
+}
+
 bool ok16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 dim3 grid_of(int64_t n4) { return dim3((unsigned)((n4 + kLanes - 1) / kLanes)); }
@@ -105,8 +156,8 @@ int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 bool ok_n4(int64_t n4) { return n4 >= 1 && n4 <= ((int64_t)1 << 36); }
 
-// One launch of ceiling `kind` (0 read, 1 copy, 2 4r3w) between the events
-// start and stop (either may be null).
+// One launch of ceiling `kind` (0 read, 1 copy, 2 4r3w, 3 4r3w_keep) between
+// the events start and stop (either may be null).
 void launch_kind(int kind, f32x4 *w, const f32x4 *g, f32x4 *m, f32x4 *v, int64_t n4, float *out,
                  hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     if (kind == 0)
@@ -115,9 +166,12 @@ void launch_kind(int kind, f32x4 *w, const f32x4 *g, f32x4 *m, f32x4 *v, int64_t
     else if (kind == 1)
         hipExtLaunchKernelGGL(ceiling_copy, grid_of(n4), dim3(kLanes), 0, stream, start, stop, 0,
                               static_cast<const f32x4 *>(w), m, n4);
-    else
+    else if (kind == 2)
         hipExtLaunchKernelGGL(ceiling_4r3w, grid_of(n4), dim3(kLanes), 0, stream, start, stop, 0,
                               w, g, m, v, n4);
+    else
+        hipExtLaunchKernelGGL(ceiling_4r3w_keep, grid_of(n4), dim3(kLanes), 0, stream, start, stop,
+                              0, w, g, m, v, n4);
 }
 
 }  // namespace
@@ -129,15 +183,16 @@ int64_t rcs_ceiling_blocks(int64_t n4) { return n4 < 1 ? 0 : read_blocks(n4); }
 
 // Average duration in microseconds of `reps` stamped launches of ceiling
 // `kind` over w, g, m, v (kind 0 reads g into out; kind 1 copies w to m;
-// kind 2 is the 4-read/3-write pattern), after two unstamped ones. Blocks
-// until they are done. Returns 0, -1 for bad arguments, -4 on a HIP error.
+// kind 2 is the 4-read/3-write pattern, kind 3 the same with cache-retaining
+// accesses on shared lines), after two unstamped ones. Blocks until they are
+// done. Returns 0, -1 for bad arguments, -4 on a HIP error.
 int rcs_ceiling_time(int kind, float *w, const float *g, float *m, float *v, int64_t n4,
                      float *out, int reps, hipStream_t stream, double *avg_us) {
-    if (kind < 0 || kind > 2 || !ok_n4(n4) || reps < 1 || reps > 1000 || avg_us == nullptr)
+    if (kind < 0 || kind > 3 || !ok_n4(n4) || reps < 1 || reps > 1000 || avg_us == nullptr)
         return -1;
     if (kind == 0 && (!ok16(g) || out == nullptr)) return -1;
     if (kind == 1 && (!ok16(w) || !ok16(m))) return -1;
-    if (kind == 2 && (!ok16(w) || !ok16(g) || !ok16(m) || !ok16(v))) return -1;
+    if (kind >= 2 && (!ok16(w) || !ok16(g) || !ok16(m) || !ok16(v))) return -1;
     f32x4 *w4 = reinterpret_cast<f32x4 *>(w), *m4 = reinterpret_cast<f32x4 *>(m);
     f32x4 *v4 = reinterpret_cast<f32x4 *>(v);
     const f32x4 *g4 = reinterpret_cast<const f32x4 *>(g);

@@ -236,7 +236,7 @@ def test_ceilings_library_loads_and_rejects_bad_arguments():
     assert [C.rcs_ceiling_blocks(k) for k in (0, 1, 2048, 2049, 1 << 30)] == [0, 1, 1, 2, 256]
     us = ctypes.c_double(-1.0)
     fake = 0x1000
-    bad = [(3, fake, fake, fake, fake, 16, fake, 10),   # no such kind
+    bad = [(4, fake, fake, fake, fake, 16, fake, 10),   # no such kind
            (-1, fake, fake, fake, fake, 16, fake, 10),
            (2, fake, fake, fake, fake, 0, fake, 10),    # no vectors
            (2, fake, fake, fake, fake, 16, fake, 0),    # no launches
