@@ -658,6 +658,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the pages time only whole training steps on other hardware: context
+        "context": {"pages_training_steps_per_min": 6,
+                    "what": "whole ANDREA-120M training step (forward, backward, update) "
+                            "on one RTX 4090 in FP16, about 10 s per step; not this metric"},
         "dtype": "f32",
         "data": f"synthetic, seeded: {wl.description}; 4 gradient buffers used in "
                 "rotation, inputs resident in HBM",
