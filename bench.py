@@ -485,16 +485,29 @@ VIEW_OFFSETS = [(0, 0, 0, 0), (0, 1, 0, 0), (0, 0, 1, 0), (0, 0, 0, 1), (1, 0, 0
                 (4, 0, 0, 0), (0, 0, 4, 4)]
 
 
-def views_leg(torch, rcs, wl, steps: int, rounds: int = 3) -> dict:
+def views_leg(torch, rcs, wl, steps: int, rounds: int = 3, only=None) -> dict:
     """The step on views of w, g, m, v at several element offsets (so at
     several 16- and 256-byte phases), with the buffers' physical placement
     held fixed: one set of padded buffers per round, every offset case timed
-    on views into the same buffers, interleaved; mean us/step per case."""
+    on views into the same buffers, interleaved; mean us/step per case.
+    only: one offset tuple to run alone, once (for counter runs)."""
     import ctypes
 
     n = wl.n
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if only is not None:
+        bufs = [torch.zeros(n + 128, device="cuda") for _ in range(4)]
+        bufs[0].normal_(0.0, 0.02)
+        bufs[1].normal_(0.0, wl.grad_sigma)
+        w, g, m, v = (b[o:o + n] for b, o in zip(bufs, only))
+        e0.record(stream)
+        for t in range(1, 1 + steps):
+            rcs.adamw_clip_step(w, g, m, v, t, wl.lr, wl.wd, wl.clip, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return {"n": n, "offsets": list(only), "steps": steps,
+                "us_per_step": e0.elapsed_time(e1) / steps * 1e3}
     times = {offs: [] for offs in VIEW_OFFSETS}
     # the bare 4-read/3-write pattern on the same buffers: all arrays on a line,
     # v 16 bytes past one with streaming accesses, and the same with
@@ -578,6 +591,8 @@ def main() -> int:
                     help="skip timing PyTorch's fused AdamW + clip on the same inputs")
     ap.add_argument("--views", action="store_true",
                     help="only time the step on views at several element offsets (fixed placement)")
+    ap.add_argument("--view-offsets", default=None, metavar="W,G,M,V",
+                    help="with --views: run only this offset case (elements), once")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -609,7 +624,13 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.views:
         rcs.lib()
-        print(json.dumps({"views": views_leg(torch, rcs, wl, args.steps)}), flush=True)
+        only = None
+        if args.view_offsets is not None:
+            only = tuple(int(x) for x in args.view_offsets.split(","))
+            if len(only) != 4 or min(only) < 0 or max(only) > 127:
+                print("--view-offsets takes four offsets 0..127", file=sys.stderr)
+                return 2
+        print(json.dumps({"views": views_leg(torch, rcs, wl, args.steps, only=only)}), flush=True)
         return 0
     rcs.lib()
     _log(f"[bench] workload {wl.name} n={n:,}: generating inputs on the device")
