@@ -19,7 +19,8 @@ from ._build import LIB as LIB_PATH
 from ._build import build
 
 __all__ = [
-    "RcsError", "adamw_clip_step", "adamw_clip_step_noalloc", "adamw_clip_step_accum", "grad_clip_inplace", "grad_zero", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
+    "RcsError", "adamw_clip_step", "adamw_clip_step_noalloc", "adamw_clip_step_accum",
+    "grad_clip_inplace", "grad_zero", "grad_global_norm", "last_grad_norm", "ckpt_bytes",
     "ckpt_pack", "ckpt_unpack", "init", "profile_enable", "profile_read",
     "strerror", "lib", "LIB_PATH", "build", "step_file_name", "MAX_N",
     "ckpt_pack_async", "ckpt_pack_wait", "CkptWriter", "StepFileCheckpointer",
@@ -77,9 +78,9 @@ def lib() -> ctypes.CDLL:
     L.adamw_clip_step_accum.argtypes = [f32p, f32p, f32p, f32p, i64, i32, f32, f32, f32, f32, vp]
     L.adamw_clip_step_accum.restype = ctypes.c_int
     L.grad_clip_inplace.argtypes = [f32p, i64, f32, vp]
+    L.grad_clip_inplace.restype = ctypes.c_int
     L.grad_zero.argtypes = [f32p, i64, vp]
     L.grad_zero.restype = ctypes.c_int
-    L.grad_clip_inplace.restype = ctypes.c_int
     L.ckpt_snapshot_bytes.argtypes = [i64]
     L.ckpt_snapshot_bytes.restype = i64
     L.ckpt_pack_async.argtypes = [i32, i64, f32p, f32p, f32p, f32p, i64, vp, i64, vp, vp]
