@@ -190,14 +190,14 @@ def test_update_parity_ragged_sizes(dev, n):
 # 256-byte boundary (64 - offset elements: bodies of exactly 4 and 7 behind a
 # 63-element head, head and tail in one block), or to the next 16-byte one when
 # fewer than 4 elements would follow (heads of 1-3, bodies of 4, 5 and 7); g, m
-# and v may sit at other 256-byte phases (1, 5, 9, 65). Arrays whose offset
-# differs from the anchor's modulo 4 (the anchor is w, or m when m and v share
-# a phase w does not) take shifted 16-byte vectors in the vector kernels
+# and v may sit at other 256-byte phases (1, 5, 9, 65). The anchor is w or m,
+# whichever shares its 128-byte line phase with more of the written arrays (m
+# only when v shares its 16-byte phase). Arrays whose offset differs from the
+# anchor's modulo 4 take shifted 16-byte vectors in the vector kernels
 # (adamw_update_mixed: every reachable combination appears here, in both
-# final-reduction forms). The anchor is w or m, whichever shares its 128-byte
-# line phase with more of the written arrays (m only when v shares its 16-byte
-# phase); arrays at the anchor's 16-byte but another line phase take aligned
-# vectors with cache-retaining accesses on the lines two waves share. Views
+# final-reduction forms); arrays at the anchor's 16-byte but another line
+# phase take aligned vectors with cache-retaining accesses on the lines two
+# waves share. Views
 # too short for either head take the scalar kernels.
 UNALIGNED_CASES = [((1, 1, 1, 1), 50_001), ((2, 2, 2, 2), 50_001), ((3, 3, 3, 3), 50_001),
                    ((1, 1, 1, 1), 67), ((1, 1, 1, 1), 70), ((2, 2, 2, 2), 66),
